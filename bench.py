@@ -1,0 +1,246 @@
+"""Benchmark of the W4A4 Hadamard-quantized linear path on one MI355X.
+
+One step = every linear of the workload, each as the two library calls of the online path:
+qv_hadamard_smooth_quant (rotate + smooth + int4 quantize, HBM-bound) then qv_w4a4_gemm (int4 GEMM
+on int8 MFMA with the dequant/GELU epilogue).  Inputs (seeded VGGT-shaped activations, packed int4
+weights, smoothing factors) are resident in HBM before the timed region; nothing is skipped inside it.
+
+Prints one JSON line: the effective TOPS of the step (2*M*N*K summed over the linears, divided by
+the step time), the GEMM kernel's fraction of the dense INT8 MFMA peak, the rotate-quantize kernel's
+fraction of HBM bandwidth, a bf16 hipBLASLt baseline on the same shapes, and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A4 linear effective TOPS + % INT8 MFMA peak at VGGT shapes"
+PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA, TOP/s
+PEAK_HBM_GBPS = 8000.0    # MI355X HBM3E, GB/s
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="block_32frames")
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
+    p.add_argument("--no-bf16-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=256, help="rows per linear in the oracle sample")
+    return p.parse_args()
+
+
+def kernel_source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bit_ptq_reconstruction_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_tag, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if taken on this source."""
+    path = os.path.join(PROFILE_DIR, f"{kernel_tag}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != src_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "requested_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_ptq_reconstruction_amd as qv
+    from bit_ptq_reconstruction_amd import synth
+    from bit_ptq_reconstruction_amd.configs import EPI_GELU, WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    qv.lib()
+    M = wl.M
+    stream = torch.cuda.current_stream()
+
+    # ---------------------------------------------------------------- resident inputs and weights
+    layers = []
+    for blk in range(wl.blocks):
+        for li, lin in enumerate(wl.linears):
+            x_seed = lin.x_seed + (1000 * blk if wl.blocks > 1 else 0)
+            w_seed = lin.w_seed + (1000 * blk if wl.blocks > 1 else 0)
+            chained = wl.chain_mlp and li > 0
+            in_dt = torch.bfloat16 if wl.in_dtype == "bf16" else torch.float32
+            X = None if chained else synth.vggt_activations_torch(M, lin.K, x_seed, in_dt, dev)
+            W = synth.weights_torch(lin.N, lin.K, w_seed, dev)
+            s = torch.empty(lin.K, device=dev)
+            inv = torch.empty(lin.K, device=dev)
+            calib = X if X is not None else synth.vggt_activations_torch(synth.FRAME_TOKENS, lin.K, x_seed, in_dt, dev)
+            qv.qv_smooth_calibrate(calib[:synth.FRAME_TOKENS], W, s, inv, 0.5)
+            Wq = torch.empty((lin.N, lin.K // 2), dtype=torch.uint8, device=dev)
+            ws = torch.empty((lin.N,), dtype=torch.float32, device=dev)
+            qv.qv_pack_weights(W, s, Wq, ws)
+            del W
+            out_dt = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
+            layers.append(dict(lin=lin, X=X, inv=inv, Wq=Wq, ws=ws,
+                               Xq=torch.empty((M, lin.K // 2), dtype=torch.uint8, device=dev),
+                               xs=torch.empty((M,), dtype=torch.float32, device=dev),
+                               Y=torch.empty((M, lin.N), dtype=out_dt, device=dev)))
+    if wl.chain_mlp:
+        for i in range(1, len(layers)):
+            layers[i]["X"] = layers[i - 1]["Y"]
+    torch.cuda.synchronize()
+
+    events = []
+
+    def step(record):
+        for L in layers:
+            if record:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record(stream)
+            qv.qv_hadamard_smooth_quant(L["X"], L["inv"], L["Xq"], L["xs"], stream)
+            if record:
+                e[1].record(stream)
+            qv.qv_w4a4_gemm(L["Xq"], L["xs"], L["Wq"], L["ws"], None, L["Y"], L["lin"].epi, stream)
+            if record:
+                e[2].record(stream)
+                events.append((L, e))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+
+    ops_per_step = sum(2.0 * M * L["lin"].N * L["lin"].K for L in layers)
+    value = ops_per_step / (wall / args.steps) / 1e12
+
+    # ---------------------------------------------------------------- per-kernel times (HIP events)
+    k1_t, k2_t, k1_bytes, k2_ops = 0.0, 0.0, 0.0, 0.0
+    per_layer = {}
+    for L, e in events:
+        lin = L["lin"]
+        t1 = e[0].elapsed_time(e[1]) * 1e-3
+        t2 = e[1].elapsed_time(e[2]) * 1e-3
+        in_b = L["X"].element_size()
+        b1 = M * lin.K * in_b + M * (lin.K // 2) + 4 * M
+        o2 = 2.0 * M * lin.N * lin.K
+        k1_t += t1
+        k2_t += t2
+        k1_bytes += b1
+        k2_ops += o2
+        d = per_layer.setdefault(lin.name, dict(n=0, k1=0.0, k2=0.0, b1=b1, o2=o2, K=lin.K, N=lin.N))
+        d["n"] += 1
+        d["k1"] += t1
+        d["k2"] += t2
+    n_launch = len(events)
+    k2_tops = k2_ops / k2_t / 1e12
+    k1_gbps = k1_bytes / k1_t / 1e9
+    kernels = {name: {"K": d["K"], "N": d["N"], "rotate_quant_us": 1e6 * d["k1"] / d["n"],
+                      "rotate_quant_GBps": d["b1"] * d["n"] / d["k1"] / 1e9,
+                      "gemm_us": 1e6 * d["k2"] / d["n"], "gemm_TOPS": d["o2"] * d["n"] / d["k2"] / 1e12}
+               for name, d in per_layer.items()}
+
+    gemm_hash = kernel_source_hash(["w4a4_gemm.hip"])
+    rq_hash = kernel_source_hash(["rotate_quant.hip", "fwht_regs.h"])
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int4", "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "M": M, "blocks": wl.blocks,
+                   "linears": [f"{l.name} {l.K}->{l.N}{' +GELU' if l.epi == EPI_GELU else ''}" for l in wl.linears],
+                   "in_dtype": wl.in_dtype, "out_dtype": wl.out_dtype, "hadamard": "K (1024 or 4096)",
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "w4a4_gemm", "bound": "mfma", "achieved": round(k2_tops, 2),
+                     "peak": PEAK_INT8_TOPS, "unit": "TOP/s", "frac": round(k2_tops / PEAK_INT8_TOPS, 4),
+                     "traffic": read_traffic("w4a4_gemm", gemm_hash),
+                     "avg_launch_us": round(1e6 * k2_t / n_launch, 3), "ops_per_launch": k2_ops / n_launch},
+        "rotate_quant_roofline": {"kernel": "rotate_quant", "bound": "hbm", "achieved": round(k1_gbps, 1),
+                                  "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(k1_gbps / PEAK_HBM_GBPS, 4),
+                                  "traffic": read_traffic("rotate_quant", rq_hash),
+                                  "avg_launch_us": round(1e6 * k1_t / n_launch, 3),
+                                  "bytes_per_launch": k1_bytes / n_launch},
+        "kernels": kernels,
+        "rotate_quant_share_of_linear_time": round(k1_t / (k1_t + k2_t), 4),
+        "gemm_only_TOPS": round(k2_tops, 2),
+        "source_hash": {"w4a4_gemm": gemm_hash, "rotate_quant": rq_hash},
+    }
+
+    # ---------------------------------------------------------------- bf16 baseline (hipBLASLt)
+    if not args.no_bf16_baseline:
+        base = []
+        for L in layers[:len(wl.linears)]:
+            lin = L["lin"]
+            Xb = synth.vggt_activations_torch(M, lin.K, 0, torch.bfloat16, dev)
+            Wb = synth.weights_torch(lin.N, lin.K, 1, dev).to(torch.bfloat16)
+            base.append((Xb, Wb, lin.epi))
+
+        def bstep():
+            for Xb, Wb, epi in base:
+                y = torch.nn.functional.linear(Xb, Wb)
+                if epi == EPI_GELU:
+                    y = torch.nn.functional.gelu(y)
+        for _ in range(args.warmup):
+            bstep()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            for _ in range(wl.blocks):
+                bstep()
+        torch.cuda.synchronize()
+        bt = (time.perf_counter() - t0) / args.steps
+        result["bf16_baseline"] = {"what": "torch.nn.functional.linear (+gelu) in bf16, same shapes",
+                                   "ms_per_step": round(1e3 * bt, 4), "TFLOPS": round(ops_per_step / bt / 1e12, 2),
+                                   "w4a4_speedup": round(bt / (wall / args.steps), 3)}
+        del base
+
+    # ---------------------------------------------------------------- CPU oracle on a bounded sample
+    if not args.no_cpu_baseline:
+        import oracle
+
+        S = min(args.cpu_rows, M)
+        t_cpu, ops_cpu = 0.0, 0.0
+        for lin in wl.linears:
+            X = synth.vggt_activations(S, lin.K, lin.x_seed, dtype=wl.in_dtype)
+            W = synth.weights(lin.N, lin.K, lin.w_seed)
+            Xh, Wh = oracle.rotate(X, oracle.ROT_FWHT), oracle.rotate(W, oracle.ROT_FWHT)
+            s, inv = oracle.smoothing(Xh, Wh, 0.5)
+            Wq, ws = oracle.pack_weights(W, s, oracle.ROT_FWHT)  # offline step: outside the timing
+            t0 = time.perf_counter()
+            oracle.w4a4_linear(X, inv, Wq, ws, None, lin.epi, oracle.ROT_EXPLICIT)
+            t_cpu += time.perf_counter() - t0
+            ops_cpu += 2.0 * S * lin.N * lin.K
+        result["cpu_baseline"] = {
+            "value": round(ops_cpu / t_cpu / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"{S} rows of each of the {len(wl.linears)} linears of one block (online step only: "
+                      f"explicit-matrix fp64 rotation, fp32 quantization, int64 triple-loop GEMM, fp64 "
+                      f"dequant/GELU), single thread, {t_cpu:.1f} s",
+            "host_cpus": os.cpu_count()}
+
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

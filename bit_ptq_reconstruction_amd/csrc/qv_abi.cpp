@@ -1,0 +1,163 @@
+// qv_abi.cpp -- the C ABI of libqv (declared in include/qv.h): host-side argument checks, then the
+// kernel launches on the caller's stream.  Every check runs before the first HIP call, so a
+// rejected call launches nothing and touches no device state.
+#include "qv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "qv_internal.h"
+
+namespace {
+
+constexpr int64_t kAlign = 16;
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
+
+int64_t dtype_bytes(qv_dtype t) { return t == QV_BF16 ? 2 : 4; }
+
+bool valid_dtype(qv_dtype t) { return t == QV_F32 || t == QV_BF16; }
+
+// Shared checks of the rotate-quantize step (activation or weight side).
+qv_status check_rotate_quant(const void* X, qv_dtype dt, int64_t rows, int64_t K, int64_t ld, const float* mult,
+                             const uint8_t* q, const float* scale) {
+  if (!valid_dtype(dt)) return QV_ERR_DTYPE;
+  if (rows < 0 || K <= 0) return QV_ERR_SHAPE;
+  if (K != 1024 && K != 4096) return QV_ERR_UNSUPPORTED;
+  if (ld < K) return QV_ERR_SHAPE;
+  if (rows == 0) return QV_OK;
+  if (!X || !q || !scale) return QV_ERR_NULL;
+  if (!aligned(X) || !aligned(q) || !aligned(mult) || ((ld * dtype_bytes(dt)) % kAlign) != 0) return QV_ERR_ALIGN;
+  return QV_OK;
+}
+
+qv_status check_gemm(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
+                     int64_t M, int64_t N, int64_t K, qv_epilogue epi, const void* Y, qv_dtype yt, int64_t ldy) {
+  if (!valid_dtype(yt) || (epi != QV_EPI_NONE && epi != QV_EPI_GELU)) return QV_ERR_DTYPE;
+  if (M < 0 || N < 0 || K <= 0) return QV_ERR_SHAPE;
+  if ((K % 128) != 0 || K > 65536 || (N % 128) != 0) return QV_ERR_UNSUPPORTED;
+  if (ldy < N) return QV_ERR_SHAPE;
+  if (M == 0 || N == 0) return QV_OK;
+  if (!Xq || !xs || !Wq || !ws || !Y) return QV_ERR_NULL;
+  if (!aligned(Xq) || !aligned(Wq) || !aligned(ws) || !aligned(bias) || !aligned(Y) ||
+      ((ldy * dtype_bytes(yt)) % kAlign) != 0)
+    return QV_ERR_ALIGN;
+  return QV_OK;
+}
+
+size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+qv_status hip_status(hipError_t e) { return e == hipSuccess ? QV_OK : QV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* qv_status_string(qv_status s) {
+  switch (s) {
+    case QV_OK: return "QV_OK";
+    case QV_ERR_NULL: return "QV_ERR_NULL: a required pointer is NULL";
+    case QV_ERR_SHAPE: return "QV_ERR_SHAPE: negative size or leading dimension smaller than the row";
+    case QV_ERR_UNSUPPORTED: return "QV_ERR_UNSUPPORTED: size outside what the kernels implement";
+    case QV_ERR_ALIGN: return "QV_ERR_ALIGN: pointer or row stride not 16-byte aligned";
+    case QV_ERR_DTYPE: return "QV_ERR_DTYPE: unknown dtype or epilogue";
+    case QV_ERR_WORKSPACE: return "QV_ERR_WORKSPACE: workspace missing or too small";
+    case QV_ERR_HIP: return "QV_ERR_HIP: HIP runtime error at launch";
+    case QV_ERR_INTERNAL: return "QV_ERR_INTERNAL: unexpected internal error";
+  }
+  return "unknown qv_status";
+}
+
+qv_status qv_hadamard_smooth_quant(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                   const float* inv_smooth, uint8_t* Xq, float* x_scale, void* hip_stream) {
+  try {
+    qv_status st = check_rotate_quant(X, x_dtype, M, K, ldx, inv_smooth, Xq, x_scale);
+    if (st != QV_OK || M == 0) return st;
+    return hip_status(qv::launch_rotate_quant(X, x_dtype == QV_BF16, M, K, ldx, inv_smooth, Xq, x_scale,
+                                              static_cast<hipStream_t>(hip_stream)));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
+qv_status qv_pack_weights(const void* W, qv_dtype w_dtype, int64_t N, int64_t K, int64_t ldw, const float* smooth,
+                          uint8_t* Wq, float* w_scale, void* hip_stream) {
+  try {
+    qv_status st = check_rotate_quant(W, w_dtype, N, K, ldw, smooth, Wq, w_scale);
+    if (st != QV_OK || N == 0) return st;
+    return hip_status(qv::launch_rotate_quant(W, w_dtype == QV_BF16, N, K, ldw, smooth, Wq, w_scale,
+                                              static_cast<hipStream_t>(hip_stream)));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
+qv_status qv_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq, const float* w_scale,
+                       const float* bias, int64_t M, int64_t N, int64_t K, qv_epilogue epi, void* Y,
+                       qv_dtype y_dtype, int64_t ldy, void* hip_stream) {
+  try {
+    qv_status st = check_gemm(Xq, x_scale, Wq, w_scale, bias, M, N, K, epi, Y, y_dtype, ldy);
+    if (st != QV_OK || M == 0 || N == 0) return st;
+    return hip_status(qv::launch_w4a4_gemm(Xq, x_scale, Wq, w_scale, bias, M, N, K, epi == QV_EPI_GELU, Y,
+                                           y_dtype == QV_BF16, ldy, static_cast<hipStream_t>(hip_stream)));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
+size_t qv_w4a4_linear_workspace_size(int64_t M, int64_t K) {
+  if (M < 0 || K <= 0 || (K % 2) != 0) return 0;
+  return round256(static_cast<size_t>(M) * static_cast<size_t>(K / 2)) + round256(static_cast<size_t>(M) * 4);
+}
+
+qv_status qv_w4a4_linear(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, int64_t ldx,
+                         const float* inv_smooth, const uint8_t* Wq, const float* w_scale, const float* bias,
+                         int64_t N, qv_epilogue epi, void* Y, qv_dtype y_dtype, int64_t ldy, void* workspace,
+                         size_t workspace_bytes, void* hip_stream) {
+  try {
+    // Validate both steps up front so that nothing is launched when either would be rejected.
+    qv_status st = check_rotate_quant(X, x_dtype, M, K, ldx, inv_smooth, reinterpret_cast<uint8_t*>(16),
+                                      reinterpret_cast<float*>(16));
+    if (st != QV_OK) return st;
+    st = check_gemm(reinterpret_cast<uint8_t*>(16), reinterpret_cast<float*>(16), Wq, w_scale, bias, M, N, K, epi,
+                    Y, y_dtype, ldy);
+    if (st != QV_OK) return st;
+    if (M == 0 || N == 0) return QV_OK;
+    const size_t need = qv_w4a4_linear_workspace_size(M, K);
+    if (!workspace || workspace_bytes < need) return QV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) % 256) != 0) return QV_ERR_ALIGN;
+    uint8_t* xq = static_cast<uint8_t*>(workspace);
+    float* xs = reinterpret_cast<float*>(xq + round256(static_cast<size_t>(M) * static_cast<size_t>(K / 2)));
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    st = hip_status(qv::launch_rotate_quant(X, x_dtype == QV_BF16, M, K, ldx, inv_smooth, xq, xs, s));
+    if (st != QV_OK) return st;
+    return hip_status(
+        qv::launch_w4a4_gemm(xq, xs, Wq, w_scale, bias, M, N, K, epi == QV_EPI_GELU, Y, y_dtype == QV_BF16, ldy, s));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
+qv_status qv_smooth_calibrate(const void* Xc, qv_dtype xc_dtype, int64_t Mc, int64_t ldx, const void* W,
+                              qv_dtype w_dtype, int64_t N, int64_t ldw, int64_t K, float alpha, float* smooth,
+                              float* inv_smooth, void* hip_stream) {
+  try {
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return QV_ERR_SHAPE;
+    if (Mc < 1 || N < 1) return QV_ERR_SHAPE;
+    qv_status st = check_rotate_quant(Xc, xc_dtype, Mc, K, ldx, nullptr, reinterpret_cast<uint8_t*>(16),
+                                      reinterpret_cast<float*>(16));
+    if (st != QV_OK) return st;
+    st = check_rotate_quant(W, w_dtype, N, K, ldw, nullptr, reinterpret_cast<uint8_t*>(16),
+                            reinterpret_cast<float*>(16));
+    if (st != QV_OK) return st;
+    if (!smooth || !inv_smooth) return QV_ERR_NULL;
+    if (!aligned(smooth) || !aligned(inv_smooth)) return QV_ERR_ALIGN;
+    return hip_status(qv::launch_smooth_calibrate(Xc, xc_dtype == QV_BF16, Mc, ldx, W, w_dtype == QV_BF16, N, ldw, K,
+                                                  alpha, smooth, inv_smooth, static_cast<hipStream_t>(hip_stream)));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,25 @@
+// qv_internal.h -- launchers shared between the kernels' translation units and the C ABI layer.
+// Arguments are validated by the ABI layer (qv_abi.cpp) before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qv {
+
+// Rotate (Hadamard width K in {1024, 4096}), multiply by mult[k] (NULL = 1), quantize each row to
+// int4 with scale absmax/7 and pack: the activation step and, with the smoothing factors as mult,
+// the weight step.
+hipError_t launch_rotate_quant(const void* X, bool bf16, int64_t M, int64_t K, int64_t ld, const float* mult,
+                               uint8_t* q, float* scale, hipStream_t st);
+
+// Int4 x int4 GEMM (N % 128 == 0, K % 128 == 0) with dequantization epilogue.
+hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws,
+                            const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out,
+                            int64_t ldy, hipStream_t st);
+
+// Smoothing factors from rotated column maxima of calibration rows and weight rows.
+hipError_t launch_smooth_calibrate(const void* Xc, bool xbf16, int64_t Mc, int64_t ldx, const void* W, bool wbf16,
+                                   int64_t N, int64_t ldw, int64_t K, float alpha, float* smooth,
+                                   float* inv_smooth, hipStream_t st);
+
+}  // namespace qv

@@ -1,0 +1,139 @@
+/*
+ * qv.h -- C ABI of libqv, an MI355X (gfx950) library for the W4A4 Hadamard-rotated, smoothed,
+ * int4-quantized linear layer of QuantVGGT.
+ *
+ * Sources, cited by page title and section:
+ *   [P4] "十亿参数的三维重建模型，能塞进手机吗？" (gslzct.com), a translation of the QuantVGGT
+ *        paper's method:  训练后量化（PTQ） -- the symmetric N-bit quantizer
+ *        q = clamp(round(x / s), -2^(N-1), 2^(N-1) - 1);  双平滑细粒度量化（DSFQ） > 预全局旋转 --
+ *        rotate activations and weights by a Hadamard matrix (H H^T = I keeps the product);
+ *        > 后局部平滑 -- per-channel smoothing factors with alpha (usually 0.5) taken from the
+ *        rotated distribution, divided out of activations and folded into weights.
+ *   [P3] the lsdiaocha.cn write-up of the paper: W4A4 (4-bit weights and activations).
+ *
+ * What one linear computes (rows of X are tokens, K is the input width and the Hadamard width):
+ *   Xhat = X . H_K / sqrt(K)                       (Sylvester-order Hadamard, K in {1024, 4096})
+ *   Xt[m][k] = Xhat[m][k] * inv_smooth[k]
+ *   x_scale[m] = max_k |Xt[m][k]| / 7,  Xq[m][k] = clamp(rne(Xt[m][k] / x_scale[m]), -8, 7)
+ *   acc[m][n] = sum_k Xq[m][k] * Wq[n][k]           (exact, int32)
+ *   Y[m][n] = acc[m][n] * x_scale[m] * w_scale[n] (+ bias[n]),  optionally GELU(y) = y * Phi(y)
+ * and the offline weight step applies the same rotation to the rows of W, multiplies by smooth[k]
+ * and quantizes per output channel.  Scales are fp32; the quantization decision is taken in fp32.
+ * A row whose fp32 scale would be zero or subnormal gets scale 0 and all-zero codes.
+ *
+ * Packed int4 layout (Xq, Wq): row-major, K/2 bytes per row, byte i of a row holds the
+ * two's-complement code of element 2i in its low nibble and of element 2i+1 in its high nibble.
+ *
+ * Conventions for every entry point:
+ *   - Array arguments are DEVICE pointers, allocated and owned by the caller.  The library allocates
+ *     nothing, frees nothing and keeps no pointer after returning.
+ *   - hip_stream is a hipStream_t passed as void* (NULL = the default stream).  Every call is
+ *     asynchronous and ordered on that stream; the library never synchronizes.
+ *   - All argument checks run on the host before any HIP call; a failed check returns its status and
+ *     launches nothing.  M == 0 (or N == 0) is a valid no-op returning QV_OK.
+ *   - Leading dimensions are in elements.  Base pointers must be 16-byte aligned and every row
+ *     stride a multiple of 16 bytes.
+ *   - Inputs must be finite; results for rows holding Inf or NaN are unspecified.
+ *   - Kernels use no atomics on the hot path; results are deterministic run to run.
+ *   - Nothing throws across the ABI.  A HIP launch error is returned as QV_ERR_HIP.
+ */
+#ifndef QV_H
+#define QV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QV_OK = 0,
+  QV_ERR_NULL = 1,        /* a required pointer is NULL */
+  QV_ERR_SHAPE = 2,       /* a size is negative, unsupported, or a leading dimension is too small */
+  QV_ERR_UNSUPPORTED = 3, /* the request is well formed but outside what the kernels implement */
+  QV_ERR_ALIGN = 4,       /* a pointer or row stride is not 16-byte aligned */
+  QV_ERR_DTYPE = 5,       /* unknown dtype or epilogue value */
+  QV_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than qv_w4a4_linear_workspace_size() */
+  QV_ERR_HIP = 7,         /* the HIP runtime reported an error when launching */
+  QV_ERR_INTERNAL = 8     /* an unexpected internal error */
+} qv_status;
+
+typedef enum { QV_F32 = 0, QV_BF16 = 1 } qv_dtype;
+
+typedef enum { QV_EPI_NONE = 0, QV_EPI_GELU = 1 } qv_epilogue;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* qv_status_string(qv_status s);
+
+/*
+ * qv_hadamard_smooth_quant -- online activation step ([P4] 预全局旋转, 后局部平滑, 训练后量化（PTQ）).
+ *   X          [M][ldx] fp32 or bf16 (x_dtype), row-major; only the first K columns are read.
+ *   K          Hadamard width = row width, 1024 or 4096 (else QV_ERR_UNSUPPORTED).
+ *   inv_smooth [K] fp32 per-channel multiplier applied after the rotation (1 / smoothing factor);
+ *              NULL means all ones (rotation only).
+ *   Xq         [M][K/2] packed int4 codes (output).
+ *   x_scale    [M] fp32 per-token scales (output).
+ */
+qv_status qv_hadamard_smooth_quant(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                   const float* inv_smooth, uint8_t* Xq, float* x_scale,
+                                   void* hip_stream);
+
+/*
+ * qv_pack_weights -- offline weight step ([P4] 预全局旋转: weights are rotated by the same H;
+ * 后局部平滑: the smoothing factor is folded into the weights).  The same kernel as the activation
+ * step, with smooth[k] as the per-channel multiplier and one output channel per row.
+ *   W       [N][ldw] fp32 or bf16 (w_dtype): row n holds output channel n over the K inputs.
+ *   K       1024 or 4096.
+ *   smooth  [K] fp32 smoothing factors s_k (NULL = ones).
+ *   Wq      [N][K/2] packed int4 codes (output);  w_scale [N] fp32 per-channel scales (output).
+ */
+qv_status qv_pack_weights(const void* W, qv_dtype w_dtype, int64_t N, int64_t K, int64_t ldw,
+                          const float* smooth, uint8_t* Wq, float* w_scale, void* hip_stream);
+
+/*
+ * qv_w4a4_gemm -- int4 x int4 contraction with int32 accumulation and a fused dequantization
+ * epilogue ([P3]: W4A4;  [P4] 训练后量化（PTQ）: symmetric scales make dequantization one product).
+ *   Xq [M][K/2], x_scale [M], Wq [N][K/2], w_scale [N] as produced by the two calls above.
+ *   bias [N] fp32 or NULL.
+ *   K  multiple of 128 in [128, 65536] (the accumulator stays exact);  N multiple of 128;  M >= 0.
+ *   epi QV_EPI_NONE or QV_EPI_GELU (GELU(y) = 0.5 y erfc(-y / sqrt 2), applied after the bias).
+ *   Y  [M][ldy] fp32 or bf16 (y_dtype, bf16 rounded to nearest even), ldy >= N.
+ */
+qv_status qv_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq, const float* w_scale,
+                       const float* bias, int64_t M, int64_t N, int64_t K, qv_epilogue epi, void* Y,
+                       qv_dtype y_dtype, int64_t ldy, void* hip_stream);
+
+/* Bytes of workspace qv_w4a4_linear needs for M rows of width K: the packed codes and the scales,
+ * each region rounded up to 256 bytes.  Returns 0 for invalid sizes. */
+size_t qv_w4a4_linear_workspace_size(int64_t M, int64_t K);
+
+/*
+ * qv_w4a4_linear -- the whole online layer: qv_hadamard_smooth_quant into the caller's workspace,
+ * then qv_w4a4_gemm.  Arguments as for those two calls; workspace is a device buffer of at least
+ * qv_w4a4_linear_workspace_size(M, K) bytes, 256-byte aligned, reused freely by later calls.
+ */
+qv_status qv_w4a4_linear(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, int64_t ldx,
+                         const float* inv_smooth, const uint8_t* Wq, const float* w_scale,
+                         const float* bias, int64_t N, qv_epilogue epi, void* Y, qv_dtype y_dtype,
+                         int64_t ldy, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * qv_smooth_calibrate -- smoothing factors from rotated statistics ([P4] 后局部平滑: the factor is
+ * computed from the distribution after the Hadamard rotation, alpha balances the two sides):
+ *   s_k = (max_m |Xhat_c[m][k]|)^alpha / (max_n |What[n][k]|)^(1 - alpha),  s_k = 1 if either max is 0,
+ *   inv_smooth[k] = 1 / s_k,
+ * where Xhat_c are the rotated calibration rows Xc [Mc][ldx] and What the rotated weight rows
+ * W [N][ldw] (both fp32 or bf16, width K in {1024, 4096}).  alpha in [0, 1].
+ *   smooth, inv_smooth  [K] fp32 outputs; both are also used as scratch by the call.
+ * Mc >= 1 and N >= 1.
+ */
+qv_status qv_smooth_calibrate(const void* Xc, qv_dtype xc_dtype, int64_t Mc, int64_t ldx, const void* W,
+                              qv_dtype w_dtype, int64_t N, int64_t ldw, int64_t K, float alpha,
+                              float* smooth, float* inv_smooth, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QV_H */

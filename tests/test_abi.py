@@ -1,0 +1,147 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point include/qv.h declares, and
+rejects bad arguments on the host before any HIP call (no device is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qv.h")
+
+QV_OK, QV_ERR_NULL, QV_ERR_SHAPE, QV_ERR_UNSUPPORTED, QV_ERR_ALIGN, QV_ERR_DTYPE, QV_ERR_WORKSPACE = range(7)
+
+P = 0x100000  # a 16-byte-aligned dummy address: never dereferenced, because validation fails first
+P_MIS = P + 4
+
+
+@pytest.fixture(scope="module")
+def L():
+    import bit_ptq_reconstruction_amd as qv
+
+    if not os.path.exists(qv.library_path()):
+        from bit_ptq_reconstruction_amd.build import build_library
+
+        build_library()
+    return qv.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:qv_status|size_t|const char\*)\s+(qv_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("qv_pack_weights", "qv_hadamard_smooth_quant", "qv_w4a4_gemm", "qv_w4a4_linear",
+              "qv_w4a4_linear_workspace_size", "qv_status_string", "qv_smooth_calibrate"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), f"libqv.so does not export {name}"
+
+
+def test_status_strings(L):
+    import bit_ptq_reconstruction_amd as qv
+
+    for s in range(9):
+        assert qv.qv_status_string(s).startswith("QV_")
+    assert "unknown" in qv.qv_status_string(99)
+
+
+def test_workspace_size(L):
+    import bit_ptq_reconstruction_amd as qv
+
+    assert qv.qv_w4a4_linear_workspace_size(1374, 1024) == 1374 * 512 + ((1374 * 4 + 255) // 256) * 256
+    assert qv.qv_w4a4_linear_workspace_size(1, 1024) == 512 + 256
+    assert qv.qv_w4a4_linear_workspace_size(-1, 1024) == 0
+    assert qv.qv_w4a4_linear_workspace_size(10, 0) == 0
+
+
+def hsq(L, X=P, dt=0, M=16, K=1024, ld=1024, mult=None, q=P, s=P):
+    return L.qv_hadamard_smooth_quant(X, dt, M, K, ld, mult, q, s, None)
+
+
+def test_rotate_quant_argument_errors(L):
+    assert hsq(L, M=0) == QV_OK                       # empty input is a no-op
+    assert hsq(L, M=0, X=None, q=None, s=None) == QV_OK
+    assert hsq(L, X=None) == QV_ERR_NULL
+    assert hsq(L, q=None) == QV_ERR_NULL
+    assert hsq(L, s=None) == QV_ERR_NULL
+    assert hsq(L, M=-1) == QV_ERR_SHAPE
+    assert hsq(L, K=2048, ld=2048) == QV_ERR_UNSUPPORTED
+    assert hsq(L, K=512, ld=512) == QV_ERR_UNSUPPORTED
+    assert hsq(L, ld=1000) == QV_ERR_SHAPE
+    assert hsq(L, dt=7) == QV_ERR_DTYPE
+    assert hsq(L, X=P_MIS) == QV_ERR_ALIGN
+    assert hsq(L, q=P_MIS) == QV_ERR_ALIGN
+    assert hsq(L, mult=P_MIS) == QV_ERR_ALIGN
+    assert hsq(L, dt=1, ld=1028) == QV_ERR_ALIGN      # bf16 row stride of 2056 bytes
+    assert L.qv_pack_weights(P, 0, 8, 4096, 4095, None, P, P, None) == QV_ERR_SHAPE
+    assert L.qv_pack_weights(P, 0, 8, 4096, 4096, None, None, P, None) == QV_ERR_NULL
+
+
+def gemm(L, Xq=P, xs=P, Wq=P, ws=P, bias=None, M=16, N=128, K=1024, epi=0, Y=P, yt=0, ldy=128):
+    return L.qv_w4a4_gemm(Xq, xs, Wq, ws, bias, M, N, K, epi, Y, yt, ldy, None)
+
+
+def test_gemm_argument_errors(L):
+    assert gemm(L, M=0) == QV_OK
+    assert gemm(L, N=0, ldy=0) == QV_OK
+    for kw in ("Xq", "xs", "Wq", "ws", "Y"):
+        assert gemm(L, **{kw: None}) == QV_ERR_NULL, kw
+    assert gemm(L, M=-3) == QV_ERR_SHAPE
+    assert gemm(L, K=1000) == QV_ERR_UNSUPPORTED
+    assert gemm(L, K=65536 * 2) == QV_ERR_UNSUPPORTED
+    assert gemm(L, N=96, ldy=96) == QV_ERR_UNSUPPORTED
+    assert gemm(L, ldy=64) == QV_ERR_SHAPE
+    assert gemm(L, epi=2) == QV_ERR_DTYPE
+    assert gemm(L, yt=3) == QV_ERR_DTYPE
+    assert gemm(L, Y=P_MIS) == QV_ERR_ALIGN
+    assert gemm(L, bias=P_MIS) == QV_ERR_ALIGN
+    assert gemm(L, Wq=P_MIS) == QV_ERR_ALIGN
+    assert gemm(L, yt=1, ldy=132) == QV_ERR_ALIGN     # bf16 row stride of 264 bytes
+
+
+def test_linear_argument_errors(L):
+    need = L.qv_w4a4_linear_workspace_size(16, 1024)
+
+    def lin(ws=P, wsb=need, **kw):
+        a = dict(X=P, dt=0, M=16, K=1024, ld=1024, inv=None, Wq=P, w_scale=P, bias=None, N=128, epi=0, Y=P,
+                 yt=0, ldy=128)
+        a.update(kw)
+        return L.qv_w4a4_linear(a["X"], a["dt"], a["M"], a["K"], a["ld"], a["inv"], a["Wq"], a["w_scale"], a["bias"],
+                                a["N"], a["epi"], a["Y"], a["yt"], a["ldy"], ws, wsb, None)
+
+    assert lin(ws=None) == QV_ERR_WORKSPACE
+    assert lin(wsb=need - 1) == QV_ERR_WORKSPACE
+    assert lin(ws=P + 16) == QV_ERR_ALIGN
+    assert lin(K=2048, ld=2048) == QV_ERR_UNSUPPORTED
+    assert lin(N=100, ldy=100) == QV_ERR_UNSUPPORTED
+    assert lin(Wq=None) == QV_ERR_NULL
+    assert lin(M=0) == QV_OK
+
+
+def test_calibrate_argument_errors(L):
+    f = ctypes.c_float
+
+    def cal(Xc=P, Mc=8, W=P, N=8, K=1024, alpha=0.5, s=P, inv=P):
+        return L.qv_smooth_calibrate(Xc, 0, Mc, K, W, 0, N, K, K, f(alpha), s, inv, None)
+
+    assert cal(alpha=1.5) == QV_ERR_SHAPE
+    assert cal(Mc=0) == QV_ERR_SHAPE
+    assert cal(N=0) == QV_ERR_SHAPE
+    assert cal(K=2048) == QV_ERR_UNSUPPORTED
+    assert cal(s=None) == QV_ERR_NULL
+    assert cal(W=None) == QV_ERR_NULL
+    assert cal(inv=P_MIS) == QV_ERR_ALIGN
+
+
+def test_binding_raises_on_error_status(L):
+    import bit_ptq_reconstruction_amd as qv
+
+    with pytest.raises(qv.QVError) as e:
+        qv._check(QV_ERR_SHAPE, "probe")
+    assert "QV_ERR_SHAPE" in str(e.value)

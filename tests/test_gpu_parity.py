@@ -1,0 +1,295 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded VGGT-shaped inputs.
+
+Rules (tests/acceptance.py): int32 accumulators bit-exact on identical codes; int4 codes
+admissible everywhere and mismatched at <= 1e-4 (only at fp32 near-ties); outputs within 1e-3
+relative error (fp32) or one bf16 ulp (bf16) of the oracle's dequantization of the GPU's codes.
+Sources: page "十亿参数的三维重建模型，能塞进手机吗？" (gslzct.com), 训练后量化（PTQ） and
+双平滑细粒度量化（DSFQ）.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import acceptance as acc
+import oracle
+from bit_ptq_reconstruction_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def qv():
+    import bit_ptq_reconstruction_amd as m
+
+    m.lib()
+    return m
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dtype, dev):
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def smoothing_for(X, W, mode=oracle.ROT_EXPLICIT):
+    """Smoothing factors from frame 0 of the activations (at most 1374 rows) and the weights."""
+    Xc = X[:min(len(X), synth.FRAME_TOKENS)]
+    return oracle.smoothing(oracle.rotate(Xc, mode), oracle.rotate(W, mode), 0.5)
+
+
+def run_quant(qv, dev, X, dtype, mult, ld_pad=0, weights=False):
+    M, K = X.shape
+    Xd = to_dev(np.pad(X, ((0, 0), (0, ld_pad))) if ld_pad else X, dtype, dev)
+    if ld_pad:
+        Xd = Xd[:, :K]
+    md = None if mult is None else torch.from_numpy(mult).to(dev)
+    q = torch.full((M, K // 2), 0xAB, dtype=torch.uint8, device=dev)
+    s = torch.full((M,), -1.0, dtype=torch.float32, device=dev)
+    (qv.qv_pack_weights if weights else qv.qv_hadamard_smooth_quant)(Xd, md, q, s)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def check_quant_against_oracle(X, mult, q_packed, s_gpu, mode, label):
+    Xhat = oracle.rotate(X, mode)
+    q_ref, s_ref = oracle.quantize_rows(Xhat, mult)
+    t, tau, _, rel_scale = acc.code_bounds(X, mult, Xhat)
+    q_gpu = oracle.unpack_int4(q_packed)
+    rate = acc.check_codes(q_gpu, q_ref, t, tau, label)
+    acc.check_scales(s_gpu, s_ref, rel_scale, label)
+    return rate, q_gpu
+
+
+# ---------------------------------------------------------------------------- rotate-quantize
+
+@pytest.mark.parametrize("K,dtype,M,smooth,pad", [
+    (1024, "fp32", 1, True, 0), (1024, "fp32", 5, False, 0), (1024, "bf16", 1374, True, 0),
+    (1024, "fp32", 1375, True, 64), (4096, "bf16", 1, True, 0), (4096, "bf16", 137, True, 0),
+    (4096, "fp32", 70, False, 32), (1024, "bf16", 257, True, 8),
+])
+def test_hadamard_smooth_quant_parity(qv, dev, K, dtype, M, smooth, pad):
+    X = synth.vggt_activations(M, K, seed=K + M, dtype=dtype)
+    W = synth.weights(128, K, seed=3)
+    mult = smoothing_for(X, W)[1] if smooth else None
+    q, s = run_quant(qv, dev, X, dtype, mult, ld_pad=pad)
+    rate, _ = check_quant_against_oracle(X, mult, q, s, oracle.ROT_EXPLICIT, f"K={K} {dtype} M={M}")
+    print(f"K={K} {dtype} M={M}: code mismatch rate {rate:.2e}")
+
+
+@pytest.mark.parametrize("K,dtype", [(1024, "fp32"), (1024, "bf16"), (4096, "bf16"), (4096, "fp32")])
+def test_pack_weights_parity(qv, dev, K, dtype):
+    N = 384
+    X = synth.vggt_activations(300, K, seed=7, dtype=dtype)
+    W = synth.weights(N, K, seed=8)
+    if dtype == "bf16":
+        W = synth.round_to_bf16(W)
+    s, _ = smoothing_for(X, W)
+    q, ws = run_quant(qv, dev, W, dtype, s, weights=True)
+    check_quant_against_oracle(W, s, q, ws, oracle.ROT_EXPLICIT, f"weights K={K} {dtype}")
+
+
+@pytest.mark.parametrize("K", [1024, 4096])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_constructed_ties_are_bit_exact(qv, dev, K, dtype):
+    """Code-space targets on half-integers: the rotated row is exactly t, the scale exactly 1, so
+    every code is round-half-even(t) with no tolerance (tests/golden/quant_ties.txt)."""
+    import scipy.linalg
+
+    t = np.array([float(r.split()[0]) for r in open(__file__.replace("test_gpu_parity.py", "golden/quant_ties.txt"))
+                  if r.strip() and not r.startswith("#")])
+    rng = np.random.default_rng(K)
+    rows = []
+    for i in range(9):
+        target = np.zeros(K)
+        pos = rng.choice(K, size=len(t), replace=False) if i else np.arange(len(t))
+        target[pos] = rng.permutation(t) if i else t
+        rows.append(target)
+    T = np.array(rows)
+    H = scipy.linalg.hadamard(K).astype(np.float64)
+    X = (T @ H) / math.sqrt(K)
+    assert np.all(X.astype(np.float32) == X) and (dtype == "fp32" or np.all(synth.round_to_bf16(X) == X))
+    q, s = run_quant(qv, dev, X.astype(np.float32), dtype, None)
+    np.testing.assert_array_equal(s, np.ones(len(rows), np.float32))
+    np.testing.assert_array_equal(oracle.unpack_int4(q), np.rint(T).astype(np.int8))
+
+
+@pytest.mark.parametrize("K", [1024, 4096])
+def test_zero_tiny_and_outlier_rows(qv, dev, K):
+    X = np.zeros((6, K), np.float32)
+    X[1, :] = 1e-41            # subnormal row: scale would be subnormal -> all-zero row
+    X[2, 17] = 1000.0          # one-hot outlier: spreads flat, every code +-7
+    X[3, :] = 2.5              # constant row: a single spike
+    X[4] = synth.vggt_activations(1, K, seed=1)[0]
+    X[5, ::2] = -3.0
+    q, s = run_quant(qv, dev, X, "fp32", None)
+    assert s[0] == 0 and s[1] == 0
+    codes = oracle.unpack_int4(q)
+    assert np.all(codes[0] == 0) and np.all(codes[1] == 0)
+    assert np.all(np.abs(codes[2]) == 7)
+    assert codes[3, 0] == 7 and np.all(codes[3, 1:] == 0)
+    check_quant_against_oracle(X, None, q, s, oracle.ROT_EXPLICIT, f"special rows K={K}")
+
+
+# ---------------------------------------------------------------------------- int4 GEMM
+
+def random_packed(rows, K, rng, fill=None):
+    if fill is None:
+        return rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    code = fill & 0xF
+    return np.full((rows, K // 2), code | (code << 4), dtype=np.uint8)
+
+
+def run_gemm(qv, dev, Xq, xs, Wq, ws, bias=None, epi=0, out="fp32", ldy_pad=0):
+    M, N = Xq.shape[0], Wq.shape[0]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    ydt = torch.float32 if out == "fp32" else torch.bfloat16
+    Yfull = torch.full((M, N + ldy_pad), float("nan"), dtype=ydt, device=dev)
+    Y = Yfull[:, :N]
+    qv.qv_w4a4_gemm(t(Xq), t(xs), t(Wq), t(ws), None if bias is None else t(bias), Y, epi)
+    torch.cuda.synchronize()
+    out_np = Y.float().cpu().numpy()
+    if ldy_pad:
+        assert torch.isnan(Yfull[:, N:].float()).all(), "wrote outside the output rows"
+    return out_np
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (37, 256, 1024), (1374, 1024, 1024), (130, 128, 4096),
+                                   (255, 384, 2048), (64, 128, 65536)])
+def test_gemm_int32_accumulators_exact(qv, dev, M, N, K):
+    """Scales of 1 and an fp32 output make Y the integer accumulator itself (|acc| < 2^24)."""
+    rng = np.random.default_rng(M * N + K)
+    Xq, Wq = random_packed(M, K, rng), random_packed(N, K, rng)
+    Y = run_gemm(qv, dev, Xq, np.ones(M, np.float32), Wq, np.ones(N, np.float32))
+    _, accum = oracle.w4a4_gemm(Xq, np.ones(M, np.float32), Wq, np.ones(N, np.float32), return_acc=True)
+    np.testing.assert_array_equal(Y, accum.astype(np.float32))
+
+
+@pytest.mark.parametrize("fa,fw", [(-8, -8), (7, 7), (7, -8), (-1, 1)])
+def test_gemm_extreme_codes(qv, dev, fa, fw):
+    rng = np.random.default_rng(0)
+    M, N, K = 129, 256, 65536
+    Xq, Wq = random_packed(M, K, rng, fa), random_packed(N, K, rng, fw)
+    Y = run_gemm(qv, dev, Xq, np.ones(M, np.float32), Wq, np.ones(N, np.float32))
+    assert np.all(Y == fa * fw * K)
+
+
+@pytest.mark.parametrize("epi,out,bias,pad", [(0, "fp32", False, 0), (1, "fp32", False, 0), (0, "bf16", False, 0),
+                                              (1, "bf16", True, 64), (0, "fp32", True, 32)])
+def test_gemm_epilogue_parity(qv, dev, epi, out, bias, pad):
+    M, N, K = 1375, 384, 1024
+    X = synth.vggt_activations(M, K, seed=5, dtype="bf16")
+    W = synth.weights(N, K, seed=6)
+    s, inv = smoothing_for(X, W)
+    Xq, xs = oracle.hadamard_smooth_quant(X, inv, oracle.ROT_FWHT)
+    Wq, ws = oracle.pack_weights(W, s, oracle.ROT_FWHT)
+    b = (0.1 * np.random.default_rng(1).standard_normal(N)).astype(np.float32) if bias else None
+    Y = run_gemm(qv, dev, Xq, xs, Wq, ws, b, epi, out, pad)
+    Y_ref = oracle.w4a4_gemm(Xq, xs, Wq, ws, b, epi)
+    worst = acc.check_outputs(Y, Y_ref, out == "bf16", f"epi={epi} out={out} bias={bias}")
+    print(f"epilogue epi={epi} out={out} bias={bias}: max rel err {worst:.2e}")
+
+
+# ---------------------------------------------------------------------------- whole layer
+
+def test_linear_equals_its_two_steps_and_is_deterministic(qv, dev):
+    M, K, N = 2000, 4096, 256
+    X = synth.vggt_activations(M, K, seed=9, dtype="bf16")
+    W = synth.weights(N, K, seed=10)
+    Xd, Wd = to_dev(X, "bf16", dev), to_dev(W, "fp32", dev)
+    sm = torch.ones(K, device=dev)
+    Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    ws = torch.empty((N,), dtype=torch.float32, device=dev)
+    qv.qv_pack_weights(Wd, sm, Wq, ws)
+    Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    xs = torch.empty((M,), dtype=torch.float32, device=dev)
+    qv.qv_hadamard_smooth_quant(Xd, sm, Xq, xs)
+    Y1 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    qv.qv_w4a4_gemm(Xq, xs, Wq, ws, None, Y1, qv.QV_EPI_GELU)
+    work = torch.empty((qv.qv_w4a4_linear_workspace_size(M, K),), dtype=torch.uint8, device=dev)
+    outs = []
+    for _ in range(3):
+        Y2 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        qv.qv_w4a4_linear(Xd, sm, Wq, ws, None, Y2, work, qv.QV_EPI_GELU)
+        outs.append(Y2)
+    torch.cuda.synchronize()
+    for Y2 in outs:
+        assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+
+
+def test_linear_against_oracle_end_to_end(qv, dev):
+    """Single 1024->1024 linear on one frame (M = 1374), fp32 in and out, smoothing from frame 0."""
+    M, K, N = 1374, 1024, 1024
+    X = synth.vggt_activations(M, K, seed=0)
+    W = synth.weights(N, K, seed=1)
+    s, inv = smoothing_for(X, W)
+    Wd = to_dev(W, "fp32", dev)
+    Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    ws = torch.empty((N,), dtype=torch.float32, device=dev)
+    qv.qv_pack_weights(Wd, torch.from_numpy(s).to(dev), Wq, ws)
+    Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    xs = torch.empty((M,), dtype=torch.float32, device=dev)
+    qv.qv_hadamard_smooth_quant(to_dev(X, "fp32", dev), torch.from_numpy(inv).to(dev), Xq, xs)
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    qv.qv_w4a4_gemm(Xq, xs, Wq, ws, None, Y)
+    torch.cuda.synchronize()
+    check_quant_against_oracle(W, s, Wq.cpu().numpy(), ws.cpu().numpy(), oracle.ROT_EXPLICIT, "weights")
+    check_quant_against_oracle(X, inv, Xq.cpu().numpy(), xs.cpu().numpy(), oracle.ROT_EXPLICIT, "activations")
+    Y_ref = oracle.w4a4_gemm(Xq.cpu().numpy(), xs.cpu().numpy(), Wq.cpu().numpy(), ws.cpu().numpy())
+    acc.check_outputs(Y.cpu().numpy(), Y_ref, False, "linear")
+    # Quantization quality (reported): relative Frobenius error against the fp64 product, next to
+    # the oracle's own W4A4 error on the same inputs (the two must agree closely).
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    err = np.linalg.norm(Y.cpu().numpy() - ref) / np.linalg.norm(ref)
+    Wq_o, ws_o = oracle.pack_weights(W, s)
+    err_o = np.linalg.norm(oracle.w4a4_linear(X, inv, Wq_o, ws_o) - ref) / np.linalg.norm(ref)
+    print(f"W4A4 relative Frobenius error vs fp64 XW^T: GPU {err:.5f}, oracle {err_o:.5f}")
+    assert abs(err - err_o) <= 1e-3 * err_o
+
+
+def test_zero_rows_give_bias_only(qv, dev):
+    M, K, N = 4, 1024, 128
+    X = np.zeros((M, K), np.float32)
+    W = synth.weights(N, K, seed=2)
+    bias = np.linspace(-1, 1, N).astype(np.float32)
+    Wq, ws = oracle.pack_weights(W)
+    Xq, xs = oracle.hadamard_smooth_quant(X)
+    Y = run_gemm(qv, dev, Xq, xs, Wq, ws, bias)
+    np.testing.assert_array_equal(Y, np.tile(bias, (M, 1)))
+
+
+def test_empty_inputs_are_noops(qv, dev):
+    K, N = 1024, 128
+    X = torch.empty((0, K), device=dev)
+    q = torch.empty((0, K // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((0,), device=dev)
+    qv.qv_hadamard_smooth_quant(X, None, q, s)
+    Wq = torch.zeros((N, K // 2), dtype=torch.uint8, device=dev)
+    ws = torch.ones((N,), device=dev)
+    Y = torch.empty((0, N), device=dev)
+    qv.qv_w4a4_gemm(q, s, Wq, ws, None, Y)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------- calibration
+
+@pytest.mark.parametrize("K,dtype", [(1024, "bf16"), (4096, "fp32")])
+def test_smooth_calibrate_parity(qv, dev, K, dtype):
+    X = synth.vggt_activations(1374, K, seed=4, dtype=dtype)
+    W = synth.weights(512, K, seed=5)
+    s_ref, inv_ref = smoothing_for(X, W, oracle.ROT_FWHT)
+    s = torch.empty(K, device=dev)
+    inv = torch.empty(K, device=dev)
+    qv.qv_smooth_calibrate(to_dev(X, dtype, dev), to_dev(W, "fp32", dev), s, inv, 0.5)
+    torch.cuda.synchronize()
+    # The column maxima carry the butterfly rounding of one element (relative <= log2(K) u sum|x| /
+    # (sqrt(K) max)), plus the fp32 pow/divide; 1e-4 relative covers both with margin on these rows.
+    np.testing.assert_allclose(s.cpu().numpy(), s_ref, rtol=1e-4)
+    np.testing.assert_allclose(inv.cpu().numpy(), inv_ref, rtol=1e-4)
