@@ -31,44 +31,58 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr float kMagic = 12582920.0f;  // 1.5 * 2^23 + 8: its low mantissa byte holds rne(t) + 8
 
-// Load the 64 values of a lane's share of one row into v (fp32 or bf16 source).
+// Raw 16-byte chunks of a lane's share of one row: 8 chunks for bf16, 16 for fp32.
+template <typename In>
+struct RawRow {
+  static constexpr int kChunks = (sizeof(In) == 2) ? 8 : 16;
+  u32x4 c[kChunks];
+};
+
 template <int K, typename In>
-__device__ __forceinline__ void load_row(const In* __restrict__ row, int lane, bool valid, float (&v)[8][8]) {
+__device__ __forceinline__ void load_raw(const In* __restrict__ row, int lane, RawRow<In>& r) {
   constexpr int C = RowLayout<K>::kChunks;
   const int c = load_chunk<K>(lane);
-  if constexpr (sizeof(In) == 2) {
-    u32x4 raw[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      raw[j] = valid ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 8 * (c + C * j)))
-                     : u32x4{0u, 0u, 0u, 0u};
+  for (int j = 0; j < 8; ++j) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(row + 8 * (c + C * j));
+    if constexpr (sizeof(In) == 2) {
+      r.c[j] = __builtin_nontemporal_load(p);
+    } else {
+      r.c[2 * j] = __builtin_nontemporal_load(p);
+      r.c[2 * j + 1] = __builtin_nontemporal_load(p + 1);
     }
+  }
+}
+
+template <typename In>
+__device__ __forceinline__ void unpack_raw(const RawRow<In>& r, float (&v)[8][8]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t w[4] = {raw[j][0], raw[j][1], raw[j][2], raw[j][3]};
+  for (int j = 0; j < 8; ++j) {
+    if constexpr (sizeof(In) == 2) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        v[j][2 * i] = __builtin_bit_cast(float, w[i] << 16);
-        v[j][2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+        const uint32_t w = r.c[j][i];
+        v[j][2 * i] = __builtin_bit_cast(float, w << 16);
+        v[j][2 * i + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
       }
-    }
-  } else {
-    f32x4 raw[16];
+    } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const f32x4* p = reinterpret_cast<const f32x4*>(row + 8 * (c + C * j));
-      raw[2 * j] = valid ? __builtin_nontemporal_load(p) : f32x4{0.f, 0.f, 0.f, 0.f};
-      raw[2 * j + 1] = valid ? __builtin_nontemporal_load(p + 1) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[j][e] = raw[2 * j][e];
-        v[j][4 + e] = raw[2 * j + 1][e];
+      for (int i = 0; i < 4; ++i) {
+        // Copy each element to a scalar before reinterpreting it: a bit-cast applied directly to
+        // a vector element reads the vector's first element.
+        const uint32_t lo = r.c[2 * j][i], hi = r.c[2 * j + 1][i];
+        v[j][i] = __builtin_bit_cast(float, lo);
+        v[j][4 + i] = __builtin_bit_cast(float, hi);
       }
     }
   }
+}
+
+template <int K, typename In>
+__device__ __forceinline__ void load_row(const In* __restrict__ row, int lane, float (&v)[8][8]) {
+  RawRow<In> r;
+  load_raw<K, In>(row, lane, r);
+  unpack_raw<In>(r, v);
 }
 
 // Eight codes (already offset by +8 in the low byte of the magic-rounded floats) -> one dword of
@@ -83,50 +97,69 @@ __device__ __forceinline__ uint32_t pack8(const uint32_t (&m)[8]) {
   return (lo | (hi << 16)) ^ 0x88888888u;  // (q + 8) ^ 8 == q & 0xF for q in [-8, 7]
 }
 
+// Per-lane multiplier table in LDS: row p holds, for the lanes at DPP-row position p (K = 1024) or
+// lane p (K = 4096), the 64 factors fold_sign * 1/sqrt(K) * mult[k] of the channels that lane owns
+// after the transform, in v[j][e] order.  Rows are padded to 68 floats so that the 16-byte reads
+// of 16 different rows fall in different banks.
+constexpr int kCmStride = 68;
+
+template <int K>
+__device__ __forceinline__ void fill_multiplier_table(const float* __restrict__ mult, float* cm) {
+  using L = RowLayout<K>;
+  constexpr int kRows = (K == 1024) ? 16 : 64;
+  for (int idx = threadIdx.x; idx < kRows * 64; idx += kThreads) {
+    const int p = idx >> 6, r = idx & 63, j = r >> 3, e = r & 7;
+    const int k = 8 * dword_index<K>(p, j) + e;
+    cm[p * kCmStride + r] = fold_sign(p) * L::kNorm * (mult ? mult[k] : 1.0f);
+  }
+}
+
 template <int K, typename In>
 __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const In* __restrict__ X, int64_t M, int64_t ldx,
                                                                const float* __restrict__ mult,
                                                                uint8_t* __restrict__ Xq,
                                                                float* __restrict__ x_scale) {
   using L = RowLayout<K>;
+  __shared__ __attribute__((aligned(16))) float cm_lds[(K == 1024 ? 16 : 64) * kCmStride];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int sub = lane / L::kLanesPerRow;  // row inside the wave
-
-  // Per-lane multiplier: fold sign * 1/sqrt(K) * smoothing multiplier of the channels this lane
-  // owns after the transform (exact: the first two factors are a signed power of two).
-  float cm[8][8];
-  const float base = fold_sign(lane) * L::kNorm;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int k0 = 8 * dword_index<K>(lane, j);
-    if (mult) {
-      const float4 a = *reinterpret_cast<const float4*>(mult + k0);
-      const float4 b = *reinterpret_cast<const float4*>(mult + k0 + 4);
-      cm[j][0] = base * a.x; cm[j][1] = base * a.y; cm[j][2] = base * a.z; cm[j][3] = base * a.w;
-      cm[j][4] = base * b.x; cm[j][5] = base * b.y; cm[j][6] = base * b.z; cm[j][7] = base * b.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) cm[j][e] = base;
-    }
-  }
+  const float* cm_row = cm_lds + (K == 1024 ? (lane & 15) : lane) * kCmStride;
 
   const int64_t groups = (M + L::kRowsPerWave - 1) / L::kRowsPerWave;
   const int64_t wave_stride = (int64_t)gridDim.x * (kThreads / 64);
-  for (int64_t g = (int64_t)blockIdx.x * (kThreads / 64) + wave; g < groups; g += wave_stride) {
+  int64_t g = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+
+  // Rows past the end are clamped to the last row (loaded, transformed, never stored), so every
+  // load is unconditional and no lane diverges before the stores.
+  auto row_of = [&](int64_t grp) {
+    const int64_t r = grp * L::kRowsPerWave + sub;
+    return r < M ? r : M - 1;
+  };
+  RawRow<In> next;
+  if (g < groups) load_raw<K, In>(X + row_of(g) * ldx, lane, next);
+
+  fill_multiplier_table<K>(mult, cm_lds);
+  __syncthreads();
+
+  for (; g < groups; g += wave_stride) {
     const int64_t row = g * L::kRowsPerWave + sub;
-    const bool valid = row < M;
     float v[8][8];
-    load_row<K, In>(X + (valid ? row : 0) * ldx, lane, valid, v);
+    unpack_raw<In>(next, v);
+    // Prefetch the next row group while this one is transformed.
+    if (g + wave_stride < groups) load_raw<K, In>(X + row_of(g + wave_stride) * ldx, lane, next);
 
     fwht_row_regs<K>(v, lane);
 
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+      const float4 c0 = *reinterpret_cast<const float4*>(cm_row + 8 * j);
+      const float4 c1 = *reinterpret_cast<const float4*>(cm_row + 8 * j + 4);
+      const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        v[j][e] *= cm[j][e];
+        v[j][e] *= c[e];
         amax = fmaxf(amax, fabsf(v[j][e]));
       }
     }
@@ -135,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const In* __rest
     if (!(s >= 1.17549435e-38f)) s = 0.0f;  // zero or subnormal scale: all-zero row
     const float r = (s > 0.0f) ? 1.0f / s : 0.0f;
 
-    if (valid) {
+    if (row < M) {
       uint32_t* out = reinterpret_cast<uint32_t*>(Xq + row * (K / 2));
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -168,10 +201,10 @@ __global__ __launch_bounds__(kThreads) void rotated_colmax_kernel(const In* __re
   const int64_t groups = (M + L::kRowsPerWave - 1) / L::kRowsPerWave;
   const int64_t wave_stride = (int64_t)gridDim.x * (kThreads / 64);
   for (int64_t g = (int64_t)blockIdx.x * (kThreads / 64) + wave; g < groups; g += wave_stride) {
-    const int64_t row = g * L::kRowsPerWave + sub;
-    const bool valid = row < M;
+    int64_t row = g * L::kRowsPerWave + sub;
+    if (row >= M) row = M - 1;  // a repeated row does not change a maximum
     float v[8][8];
-    load_row<K, In>(X + (valid ? row : 0) * ld, lane, valid, v);
+    load_row<K, In>(X + row * ld, lane, v);
     fwht_row_regs<K>(v, lane);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -206,17 +239,34 @@ __global__ void zero_kernel(unsigned* __restrict__ p, int64_t n) {
   if (i < n) p[i] = 0u;
 }
 
-int grid_for_rows(int64_t M, int rows_per_wave) {
+// Resident blocks per CU for a kernel (queried once per kernel and device) times the CU count:
+// the streaming kernels loop over row groups, so a grid of exactly the resident blocks keeps every
+// wave busy with prefetched rows and leaves no partial last round.
+template <auto kKernel>
+int resident_grid() {
+  static int cached[16] = {0};  // one cache per kernel instance (the template argument) and device
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  if (cached[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kKernel, kThreads, 0) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    cached[dev] = per_cu * cus;
+  }
+  return cached[dev];
+}
+
+int grid_for_rows(int64_t M, int rows_per_wave, int resident) {
   const int64_t groups = (M + rows_per_wave - 1) / rows_per_wave;
   const int64_t blocks = (groups + (kThreads / 64) - 1) / (kThreads / 64);
-  const int64_t cap = 256 * 8;  // enough resident waves to cover HBM latency; rows loop beyond
-  return (int)(blocks < cap ? blocks : cap);
+  return (int)(blocks < resident ? blocks : resident);
 }
 
 template <int K, typename In>
 hipError_t launch_rq(const void* X, int64_t M, int64_t ld, const float* mult, uint8_t* q, float* scale,
                      hipStream_t st) {
-  const int grid = grid_for_rows(M, RowLayout<K>::kRowsPerWave);
+  const int grid = grid_for_rows(M, RowLayout<K>::kRowsPerWave, resident_grid<rotate_quant_kernel<K, In>>());
   hipLaunchKernelGGL((rotate_quant_kernel<K, In>), dim3(grid), dim3(kThreads), 0, st,
                      static_cast<const In*>(X), M, ld, mult, q, scale);
   return hipGetLastError();
@@ -224,7 +274,7 @@ hipError_t launch_rq(const void* X, int64_t M, int64_t ld, const float* mult, ui
 
 template <int K, typename In>
 hipError_t launch_colmax(const void* X, int64_t M, int64_t ld, unsigned* colmax, hipStream_t st) {
-  const int grid = grid_for_rows(M, RowLayout<K>::kRowsPerWave);
+  const int grid = grid_for_rows(M, RowLayout<K>::kRowsPerWave, resident_grid<rotated_colmax_kernel<K, In>>());
   hipLaunchKernelGGL((rotated_colmax_kernel<K, In>), dim3(grid), dim3(kThreads), 0, st,
                      static_cast<const In*>(X), M, ld, colmax);
   return hipGetLastError();

@@ -5,19 +5,29 @@
 // QuantVGGT paper) with symmetric per-token / per-output-channel scales ("十亿参数的三维重建模型，
 // 能塞进手机吗？" (gslzct.com), 训练后量化（PTQ）), so y = acc * x_scale[m] * w_scale[n].
 //
-// Data path.  Packed int4 tiles of Wq (rows n) and Xq (rows m) go global -> registers -> LDS
-// (double buffered, XOR-swizzled at 8-byte granularity so the fragment reads spread over the banks).
-// Each wave reads 8 packed bytes per lane per 16 x 64 operand fragment and widens them to int8 with
-// two masks: (p & 0xF0F0F0F0) keeps the odd-k nibbles as 16 * q and ((p << 4) & 0xF0F0F0F0) the
-// even-k ones.  Both operands carry the factor 16, so the int32 accumulator holds 256 * acc (exact:
-// |256 * acc| <= 256 * 64 * 65536 < 2^31) and an arithmetic shift by 8 recovers acc.  Because A
-// and B are widened identically, the order of k inside a fragment is the same for both, and a dot
-// product does not depend on the order of its terms.
-// Operand roles: the MFMA A operand is the weight tile (output rows i = n) and B the activation
-// tile (output columns j = m); a lane then owns four consecutive n of one m and stores them with
-// one 16-byte (fp32) or 8-byte (bf16) write.
+// Block tile BN (weight rows n) x BM (token rows m), four waves in a 2 x 2 grid; each wave owns a
+// (BN/2) x (BM/2) sub-tile of v_mfma_i32_32x32x32_i8 fragments whose int32 accumulators live in
+// the AGPR file.  Per stage of 128 codes (64 bytes of every tile row):
+//   * each wave issues global_load_lds_dwordx4 for its share of both packed tiles (no registers,
+//     no LDS store instructions) into a ring of STAGES buffers, STAGES - 1 stages ahead; the
+//     16-byte units of a 64-byte tile row are stored XOR-swizzled (unit u of row r at
+//     u ^ ((r ^ r >> 2) & 3)) so the fragment reads hit distinct banks;
+//   * a fragment is two ds_read_b128 per lane (32 + 32 packed codes), feeding four MFMAs;
+//   * codes are widened to int8 with two masks: (p & 0xF0F0F0F0) keeps the odd-k nibbles as 16 q
+//     and ((p << 4) & 0xF0F0F0F0) the even-k ones.  Both operands carry the factor 16, so the
+//     accumulator holds 256 * acc (exact: |256 acc| <= 256 * 64 * 65536 < 2^31) and an arithmetic
+//     shift by 8 recovers acc.  A and B are widened the same way, so every k is paired with itself
+//     and the order of the terms inside a fragment does not matter;
+//   * the widening of the next operands is interleaved with the MFMAs (three VALU ops per MFMA), so
+//     the unpack runs on the vector ALU while the matrix core is busy.
+// MFMA operand roles: A = weight tile (output rows i = n), B = activation tile (columns j = m): a
+// lane owns runs of four consecutive n of one m and writes each with one 8-byte (bf16) or 16-byte
+// (fp32) store.  Tiles are assigned XCD-major: the hardware deals blocks round-robin over the 8
+// XCDs, and the block -> tile map gives each XCD a contiguous run of tiles sharing activation rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "qv_internal.h"
 
@@ -26,37 +36,62 @@ namespace qv {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+#ifndef QV_STAGES
+#define QV_STAGES 3  // LDS ring depth of the GEMM main loop
+#endif
 
 constexpr int kThreads = 256;
-constexpr int kTileN = 128;         // weight rows per block
-constexpr int kTileM = 128;         // token rows per block
-constexpr int kTileKBytes = 64;     // 128 int4 codes per row per stage
-constexpr int kWaveN = 64, kWaveM = 64;
-constexpr int kFragN = kWaveN / 16, kFragM = kWaveM / 16;
+constexpr int kRowBytes = 64;  // packed bytes of one tile row per stage (128 codes)
+constexpr int kXcds = 8;
 
-// Byte offset of 8-byte unit u of tile row r inside an LDS tile (64 bytes per row).
-__device__ __forceinline__ int lds_off(int r, int u) { return r * kTileKBytes + 8 * (u ^ ((r >> 1) & 7)); }
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 2)) & 3; }
 
-__device__ __forceinline__ v4i widen(uint2 p) {
+__device__ __forceinline__ v4i widen(uint32_t p0, uint32_t p1) {
   v4i o;
-  o[0] = (int)((p.x << 4) & 0xF0F0F0F0u);
-  o[1] = (int)(p.x & 0xF0F0F0F0u);
-  o[2] = (int)((p.y << 4) & 0xF0F0F0F0u);
-  o[3] = (int)(p.y & 0xF0F0F0F0u);
+  o[0] = (int)((p0 << 4) & 0xF0F0F0F0u);
+  o[1] = (int)(p0 & 0xF0F0F0F0u);
+  o[2] = (int)((p1 << 4) & 0xF0F0F0F0u);
+  o[3] = (int)(p1 & 0xF0F0F0F0u);
   return o;
 }
 
-__device__ __forceinline__ float gelu(float y) { return 0.5f * y * erfcf(-0.70710678118654752f * y); }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  // Round to nearest even (finite inputs).
-  uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
-  ua = (ua + 0x7FFFu + ((ua >> 16) & 1u)) >> 16;
-  ub = (ub + 0x7FFFu + ((ub >> 16) & 1u)) & 0xFFFF0000u;
-  return ua | ub;
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <bool kBF16Out, bool kGelu>
+// GELU(y) = y * Phi(y) with Phi(-|y|) = erfc(|y| / sqrt 2) / 2, erfc from the Chebyshev-fitted
+// approximation of Numerical Recipes (Press et al., "erfcc": fractional error below 1.2e-7 on the
+// whole real line).  In fp32 the largest relative error of this GELU is about 2.4e-5, down to the
+// smallest normal output.
+__device__ __forceinline__ float gelu(float y) {
+  const float z = fabsf(y) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
+  float p = 0.17087277f;
+  p = __builtin_fmaf(p, t, -0.82215223f);
+  p = __builtin_fmaf(p, t, 1.48851587f);
+  p = __builtin_fmaf(p, t, -1.13520398f);
+  p = __builtin_fmaf(p, t, 0.27886807f);
+  p = __builtin_fmaf(p, t, -0.18628806f);
+  p = __builtin_fmaf(p, t, 0.09678418f);
+  p = __builtin_fmaf(p, t, 0.37409196f);
+  p = __builtin_fmaf(p, t, 1.00002368f);
+  p = __builtin_fmaf(p, t, -1.26551223f);
+  // te = 2^24 erfc(z): the exponent carries a +24 so that exp(-z^2) stays a normal number wherever
+  // y * Phi(y) is one; the factor 2^-25 = 2^-24 / 2 is applied after the product with y.
+  const float te = t * __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fmaf(-z, z, p), 1.44269504088896341f, 24.0f));
+  return (y < 0.0f) ? (y * te) * 2.98023223876953125e-08f : y * __builtin_fmaf(te, -2.98023223876953125e-08f, 1.0f);
+}
+
+template <int BN, int BM, int STAGES, bool kBF16Out, bool kGelu>
 __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(const uint8_t* __restrict__ Xq,
                                                             const float* __restrict__ x_scale,
                                                             const uint8_t* __restrict__ Wq,
@@ -64,134 +99,214 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(const uint8_t* __re
                                                             const float* __restrict__ bias, int64_t M,
                                                             int64_t N, int64_t K, void* __restrict__ Y,
                                                             int64_t ldy) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileN * kTileKBytes];  // [buf][A/B][...]
+  constexpr int WN = BN / 2, WM = BM / 2;  // wave sub-tile
+  constexpr int FN = WN / 32, FM = WM / 32;
+  constexpr int kUnits = (BN + BM) * (kRowBytes / 16);  // 16-byte units per stage
+  constexpr int kLoads = kUnits / kThreads;              // LDS-direct loads per lane per stage
+  constexpr int kStageBytes = (BN + BM) * kRowBytes;
+  static_assert(kUnits % kThreads == 0, "tile must split evenly over the waves");
+  static_assert(STAGES >= 2 && (STAGES - 2) * kLoads < 64, "pipeline depth");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
 
-  const int64_t tiles_n = N / kTileN;
-  const int64_t tile_n = blockIdx.x % tiles_n;
-  const int64_t tile_m = blockIdx.x / tiles_n;
-  const int64_t n0 = tile_n * kTileN;
-  const int64_t m0 = tile_m * kTileM;
+  // XCD-major tile order.
+  const int64_t tiles_n = N / BN;
+  const int64_t tiles = tiles_n * ((M + BM - 1) / BM);
+  const int64_t b = blockIdx.x;
+  const int64_t per = tiles / kXcds, rem = tiles % kXcds;
+  const int64_t xcd = b % kXcds, local = b / kXcds;
+  const int64_t tile = xcd * per + (xcd < rem ? xcd : rem) + local;
+  const int64_t tile_n = tile % tiles_n;
+  const int64_t tile_m = tile / tiles_n;
+  const int64_t n0 = tile_n * BN;
+  const int64_t m0 = tile_m * BM;
   const int64_t row_bytes = K / 2;
 
-  // Global -> register staging: each thread moves two 16-byte chunks of each tile per stage.
-  const uint8_t* gA[2];
-  const uint8_t* gB[2];
-  int lrow[2], lunit[2];
+  // Source of each of this lane's loads; LDS unit P = 64 * (4 i + wave) + lane of the stage buffer.
+  const uint8_t* src[kLoads];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + kThreads * i;  // 512 chunks of 16 bytes per tile
-    lrow[i] = c >> 2;
-    lunit[i] = (c & 3) * 2;
-    gA[i] = Wq + (n0 + lrow[i]) * row_bytes + (c & 3) * 16;
-    int64_t mr = m0 + lrow[i];
-    if (mr > M - 1) mr = M - 1;  // ragged tail: duplicate the last row; its outputs are not stored
-    gB[i] = Xq + mr * row_bytes + (c & 3) * 16;
+  for (int i = 0; i < kLoads; ++i) {
+    const int P = 64 * (4 * i + wave) + lane;
+    const int r = P >> 2;  // row inside the combined A|B tile
+    if (r < BN) {
+      src[i] = Wq + (n0 + r) * row_bytes + 16 * ((P & 3) ^ swz(r));
+    } else {
+      const int rb = r - BN;
+      int64_t mr = m0 + rb;
+      if (mr > M - 1) mr = M - 1;  // ragged tail: repeat the last row; its outputs are not stored
+      src[i] = Xq + mr * row_bytes + 16 * ((P & 3) ^ swz(rb));
+    }
   }
-  uint4 stA[2], stB[2];
-  auto gload = [&](int64_t kb) {
+  auto issue_stage = [&](int buf, int64_t kb) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      stA[i] = *reinterpret_cast<const uint4*>(gA[i] + kb);
-      stB[i] = *reinterpret_cast<const uint4*>(gB[i] + kb);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      uint8_t* a = &lds[buf][0][0];
-      uint8_t* b = &lds[buf][1][0];
-      *reinterpret_cast<uint2*>(a + lds_off(lrow[i], lunit[i])) = make_uint2(stA[i].x, stA[i].y);
-      *reinterpret_cast<uint2*>(a + lds_off(lrow[i], lunit[i] + 1)) = make_uint2(stA[i].z, stA[i].w);
-      *reinterpret_cast<uint2*>(b + lds_off(lrow[i], lunit[i])) = make_uint2(stB[i].x, stB[i].y);
-      *reinterpret_cast<uint2*>(b + lds_off(lrow[i], lunit[i] + 1)) = make_uint2(stB[i].z, stB[i].w);
+    for (int i = 0; i < kLoads; ++i) {
+      uint8_t* dst = lds + buf * kStageBytes + 1024 * (4 * i + wave);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[i] + kb),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                           reinterpret_cast<uintptr_t>(dst)),
+                                       16, 0, 0);
     }
   };
 
-  v4i acc[kFragN][kFragM];
+  v16i acc[FN][FM];
 #pragma unroll
-  for (int a = 0; a < kFragN; ++a)
+  for (int a = 0; a < FN; ++a)
 #pragma unroll
-    for (int b = 0; b < kFragM; ++b) acc[a][b] = v4i{0, 0, 0, 0};
+    for (int c = 0; c < FM; ++c) acc[a][c] = v16i{};
 
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
-  const int nk = (int)(K / (2 * kTileKBytes));
+  const int r32 = lane & 31;
+  const int h = lane >> 5;
+  const int nk = (int)(K / (2 * kRowBytes));
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue_stage(s, (int64_t)s * kRowBytes);
 
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((int64_t)(kt + 1) * kTileKBytes);
-    const uint8_t* As = &lds[cur][0][0];
-    const uint8_t* Bs = &lds[cur][1][0];
+    // Stage kt has landed once at most STAGES - 2 later stages are still in flight.
+    if (kt + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * kLoads>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // every wave's share of stage kt is in LDS; stage kt - 1 is consumed
+    if (kt + STAGES - 1 < nk) issue_stage((kt + STAGES - 1) % STAGES, (int64_t)(kt + STAGES - 1) * kRowBytes);
+
+    const uint8_t* As = lds + (kt % STAGES) * kStageBytes;
+    const uint8_t* Bs = As + BN * kRowBytes;
+    u32x4 pa[FN][2], pb[FM][2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int u = 4 * s + g;  // 8-byte unit of this lane inside the 64-byte row chunk
-      v4i fa[kFragN], fb[kFragM];
+    for (int a = 0; a < FN; ++a) {
+      const int r = wn * WN + 32 * a + r32;
 #pragma unroll
-      for (int a = 0; a < kFragN; ++a)
-        fa[a] = widen(*reinterpret_cast<const uint2*>(As + lds_off(wn * kWaveN + 16 * a + r16, u)));
-#pragma unroll
-      for (int b = 0; b < kFragM; ++b)
-        fb[b] = widen(*reinterpret_cast<const uint2*>(Bs + lds_off(wm * kWaveM + 16 * b + r16, u)));
-#pragma unroll
-      for (int a = 0; a < kFragN; ++a)
-#pragma unroll
-        for (int b = 0; b < kFragM; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[a], fb[b], acc[a][b], 0, 0, 0);
+      for (int q = 0; q < 2; ++q)
+        pa[a][q] = *reinterpret_cast<const u32x4*>(As + r * kRowBytes + 16 * ((2 * q + h) ^ swz(r)));
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < FM; ++c) {
+      const int r = wm * WM + 32 * c + r32;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        pb[c][q] = *reinterpret_cast<const u32x4*>(Bs + r * kRowBytes + 16 * ((2 * q + h) ^ swz(r)));
+    }
+    // Four K32 sub-steps: sub-step s uses dwords 2(s&1), 2(s&1)+1 of read q = s >> 1.
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v4i fa[FN];
+#pragma unroll
+      for (int a = 0; a < FN; ++a) {
+        const uint32_t p0 = pa[a][s >> 1][2 * (s & 1)], p1 = pa[a][s >> 1][2 * (s & 1) + 1];
+        fa[a] = widen(p0, p1);
+      }
+#pragma unroll
+      for (int c = 0; c < FM; ++c) {
+        const uint32_t p0 = pb[c][s >> 1][2 * (s & 1)], p1 = pb[c][s >> 1][2 * (s & 1) + 1];
+        const v4i fb = widen(p0, p1);
+#pragma unroll
+        for (int a = 0; a < FN; ++a) acc[a][c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[a], fb, acc[a][c], 0, 0, 0);
+      }
+    }
+    // Schedule: the fragment reads, the first sub-step's widening, then one MFMA per three VALU
+    // ops so the remaining widening overlaps the matrix core.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * (FN + FM), 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6 * (FN + FM), 0);
+#pragma unroll
+    for (int i = 0; i < 6 * (FN + FM); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * FN * FM, 0);
   }
 
-  // Epilogue: lane owns n = n0 + wn*64 + 16a + 4g + (0..3), m = m0 + wm*64 + 16b + r16.
+  // Epilogue.  The lane holds, for fragment (a, c) and register group vg, outputs
+  // m = wm*WM + 32c + r32 and n = wn*WN + 32a + 8vg + 4h + (0..3) of the tile.  They are dequantized
+  // (+ bias) (+ GELU), converted, and staged in LDS as the wave's WM x WN output block (rows padded
+  // by 8 or 16 bytes so the staging writes spread over the banks); the block is then written with
+  // 16-byte non-temporal stores, each group of lanes covering whole contiguous row segments.
+  using OutT = typename std::conditional<kBF16Out, uint16_t, float>::type;
+  constexpr int kOutRowBytes = WN * (int)sizeof(OutT) + (kBF16Out ? 8 : 16);
+  __syncthreads();  // every wave is done with the stage buffers
+  uint8_t* stage_out = lds + wave * (WM * kOutRowBytes);
+  float sa[FM];
 #pragma unroll
-  for (int b = 0; b < kFragM; ++b) {
-    const int64_t m = m0 + wm * kWaveM + 16 * b + r16;
-    if (m >= M) continue;
-    const float sa = x_scale[m];
+  for (int c = 0; c < FM; ++c) {
+    const int64_t m = m0 + wm * WM + 32 * c + r32;
+    sa[c] = x_scale[m < M ? m : M - 1];
+  }
 #pragma unroll
-    for (int a = 0; a < kFragN; ++a) {
-      const int64_t n = n0 + wn * kWaveN + 16 * a + 4 * g;
-      const float4 sw = *reinterpret_cast<const float4*>(w_scale + n);
-      float y[4];
-      const float swv[4] = {sw.x, sw.y, sw.z, sw.w};
+  for (int a = 0; a < FN; ++a) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) y[v] = (float)(acc[a][b][v] >> 8) * sa * swv[v];
-      if (bias) {
-        const float4 bv = *reinterpret_cast<const float4*>(bias + n);
-        y[0] += bv.x; y[1] += bv.y; y[2] += bv.z; y[3] += bv.w;
+    for (int vg = 0; vg < 4; ++vg) {
+      const int nl = 32 * a + 8 * vg + 4 * h;  // column inside the wave block
+      const int64_t n = n0 + wn * WN + nl;
+      const float4 sw4 = *reinterpret_cast<const float4*>(w_scale + n);
+      const float4 b4 = bias ? *reinterpret_cast<const float4*>(bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float sw[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
+      const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int c = 0; c < FM; ++c) {
+        const int ml = 32 * c + r32;  // row inside the wave block
+        float y[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          y[v] = (float)(acc[a][c][4 * vg + v] >> 8) * sa[c] * sw[v] + bb[v];
+          if constexpr (kGelu) y[v] = gelu(y[v]);
+        }
+        uint8_t* dst = stage_out + ml * kOutRowBytes + nl * (int)sizeof(OutT);
+        if constexpr (kBF16Out) {
+          const bf16x2 lo = __builtin_convertvector((f32x2{y[0], y[1]}), bf16x2);
+          const bf16x2 hi = __builtin_convertvector((f32x2{y[2], y[3]}), bf16x2);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+        }
       }
-      if constexpr (kGelu) {
+    }
+  }
+  // Wave-local: the block written above is read back by the same wave only.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int kChunksPerRow = WN * (int)sizeof(OutT) / 16;  // 16-byte chunks per row
+  constexpr int kRowsPerPass = 64 / kChunksPerRow;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) y[v] = gelu(y[v]);
-      }
-      if constexpr (kBF16Out) {
-        uint16_t* out = static_cast<uint16_t*>(Y) + m * ldy + n;
-        *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-      } else {
-        float* out = static_cast<float*>(Y) + m * ldy + n;
-        *reinterpret_cast<float4*>(out) = make_float4(y[0], y[1], y[2], y[3]);
-      }
+  for (int pass = 0; pass < WM / kRowsPerPass; ++pass) {
+    const int ml = pass * kRowsPerPass + lane / kChunksPerRow;
+    const int ch = lane % kChunksPerRow;
+    const int64_t m = m0 + wm * WM + ml;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage_out + ml * kOutRowBytes + 16 * ch);
+    if (m < M) {
+      uint8_t* out = reinterpret_cast<uint8_t*>(static_cast<OutT*>(Y) + m * ldy + n0 + wn * WN) + 16 * ch;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out));
     }
   }
 }
 
-template <bool kBF16Out, bool kGelu>
+template <int BN, int BM, int STAGES, bool kBF16Out, bool kGelu>
 hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
                     int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
-  const int64_t blocks = (N / kTileN) * ((M + kTileM - 1) / kTileM);
-  hipLaunchKernelGGL((w4a4_gemm_kernel<kBF16Out, kGelu>), dim3((unsigned)blocks), dim3(kThreads), 0, st, Xq, xs,
-                     Wq, ws, bias, M, N, K, Y, ldy);
+  constexpr size_t kStageLds = (size_t)STAGES * (BN + BM) * kRowBytes;
+  constexpr size_t kOutLds = 4 * (size_t)(BM / 2) * ((BN / 2) * (kBF16Out ? 2 : 4) + (kBF16Out ? 8 : 16));
+  constexpr size_t kLds = kStageLds > kOutLds ? kStageLds : kOutLds;
+  static int attr_set[16] = {0};  // per device: allow more than 64 KB of dynamic LDS once
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  if (!attr_set[dev]) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a4_gemm_kernel<BN, BM, STAGES, kBF16Out, kGelu>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    if (e != hipSuccess) return e;
+    attr_set[dev] = 1;
+  }
+  const int64_t blocks = (N / BN) * ((M + BM - 1) / BM);
+  hipLaunchKernelGGL((w4a4_gemm_kernel<BN, BM, STAGES, kBF16Out, kGelu>), dim3((unsigned)blocks), dim3(kThreads), kLds,
+                     st, Xq, xs, Wq, ws, bias, M, N, K, Y, ldy);
   return hipGetLastError();
 }
+
+// 128 x 128 tiles (64 x 64 per wave): about 160 registers per lane and 48 KB of LDS, so three
+// blocks share a CU and one block's barrier, prologue and epilogue overlap another's MFMAs.
+constexpr int kTileN = 128, kTileM = 128;
 
 }  // namespace
 
@@ -199,11 +314,11 @@ hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* xs, const uint8_t* W
                             const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out,
                             int64_t ldy, hipStream_t st) {
   if (bf16_out) {
-    return gelu ? launch_t<true, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
-                : launch_t<true, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+    return gelu ? launch_t<kTileN, kTileM, QV_STAGES, true, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
+                : launch_t<kTileN, kTileM, QV_STAGES, true, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
   }
-  return gelu ? launch_t<false, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
-              : launch_t<false, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+  return gelu ? launch_t<kTileN, kTileM, QV_STAGES, false, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
+              : launch_t<kTileN, kTileM, QV_STAGES, false, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
 }
 
 }  // namespace qv
