@@ -37,6 +37,9 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
     p.add_argument("--no-bf16-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=256, help="rows per linear in the oracle sample")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="before the timed steps, copy this many MiB device-to-device once (a plain copy "
+                        "of known size that calibrates the HBM byte counters of a profiling run)")
     return p.parse_args()
 
 
@@ -108,6 +111,15 @@ def main():
         for i in range(1, len(layers)):
             layers[i]["X"] = layers[i - 1]["Y"]
     torch.cuda.synchronize()
+
+    if args.copy_probe_mib > 0:
+        nbytes = args.copy_probe_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     events = []
 
