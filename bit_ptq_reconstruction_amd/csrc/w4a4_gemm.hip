@@ -42,14 +42,27 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #ifndef QV_STAGES
-#define QV_STAGES 3  // LDS ring depth of the GEMM main loop
+#define QV_STAGES 3  // LDS ring depth of the GEMM main loop, 128 codes per stage
+#endif
+#ifndef QV_RB128
+#define QV_RB128 0
+#endif
+#ifndef QV_DMA
+#define QV_DMA 1  // 1: LDS-DMA stage loads; 0: loads through registers and ds_write_b128
+#endif
+#ifndef QV_STAGES_128
+#define QV_STAGES_128 2  // ring depth with 256 codes per stage
 #endif
 
 constexpr int kThreads = 256;
-constexpr int kRowBytes = 64;  // packed bytes of one tile row per stage (128 codes)
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 2)) & 3; }
+// XOR swizzle of the 16-byte units of a tile row (U units per row): conflict-free fragment reads
+// whether the LDS serves 8 lanes per 128 bytes or 16 lanes per 256 bytes.
+template <int U>
+__device__ __forceinline__ int swz(int r) {
+  return (U == 4) ? ((r ^ (r >> 2)) & 3) : ((r ^ (r >> 3)) & 7);
+}
 
 __device__ __forceinline__ v4i widen(uint32_t p0, uint32_t p1) {
   v4i o;
@@ -91,8 +104,8 @@ __device__ __forceinline__ float gelu(float y) {
   return (y < 0.0f) ? (y * te) * 2.98023223876953125e-08f : y * __builtin_fmaf(te, -2.98023223876953125e-08f, 1.0f);
 }
 
-template <int BN, int BM, int STAGES, bool kBF16Out, bool kGelu>
-__global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(const uint8_t* __restrict__ Xq,
+template <int BN, int BM, int RB, int STAGES, bool kBF16Out, bool kGelu>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 128 ? 2 : 3))) void w4a4_gemm_kernel(const uint8_t* __restrict__ Xq,
                                                             const float* __restrict__ x_scale,
                                                             const uint8_t* __restrict__ Wq,
                                                             const float* __restrict__ w_scale,
@@ -101,7 +114,11 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(const uint8_t* __re
                                                             int64_t ldy) {
   constexpr int WN = BN / 2, WM = BM / 2;  // wave sub-tile
   constexpr int FN = WN / 32, FM = WM / 32;
-  constexpr int kUnits = (BN + BM) * (kRowBytes / 16);  // 16-byte units per stage
+  constexpr int kRowBytes = RB;   // packed bytes of one tile row per stage (2 RB codes)
+  constexpr int U = RB / 16;      // 16-byte units per tile row and stage
+  constexpr int kSub = RB / 16;   // K32 MFMA sub-steps per stage
+  constexpr int kReads = RB / 32; // ds_read_b128 per fragment per stage
+  constexpr int kUnits = (BN + BM) * U;  // 16-byte units per stage
   constexpr int kLoads = kUnits / kThreads;              // LDS-direct loads per lane per stage
   constexpr int kStageBytes = (BN + BM) * kRowBytes;
   static_assert(kUnits % kThreads == 0, "tile must split evenly over the waves");
@@ -131,16 +148,29 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(const uint8_t* __re
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const int P = 64 * (4 * i + wave) + lane;
-    const int r = P >> 2;  // row inside the combined A|B tile
+    const int r = P / U;  // row inside the combined A|B tile
     if (r < BN) {
-      src[i] = Wq + (n0 + r) * row_bytes + 16 * ((P & 3) ^ swz(r));
+      src[i] = Wq + (n0 + r) * row_bytes + 16 * ((P % U) ^ swz<U>(r));
     } else {
       const int rb = r - BN;
       int64_t mr = m0 + rb;
       if (mr > M - 1) mr = M - 1;  // ragged tail: repeat the last row; its outputs are not stored
-      src[i] = Xq + mr * row_bytes + 16 * ((P & 3) ^ swz(rb));
+      src[i] = Xq + mr * row_bytes + 16 * ((P % U) ^ swz<U>(rb));
     }
   }
+  // Stage loads.  With LDS-DMA (global_load_lds_dwordx4) the 16 bytes of lane l land at unit
+  // 64 * (4 i + wave) + l of the stage buffer directly; otherwise they are fetched into registers
+  // (fetch_stage) and written to the same units with ds_write_b128 (store_stage).
+  u32x4 staged[kLoads];
+  auto fetch_stage = [&](int64_t kb) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) staged[i] = *reinterpret_cast<const u32x4*>(src[i] + kb);
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+      *reinterpret_cast<u32x4*>(lds + buf * kStageBytes + 1024 * (4 * i + wave) + 16 * lane) = staged[i];
+  };
   auto issue_stage = [&](int buf, int64_t kb) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
@@ -151,6 +181,7 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(const uint8_t* __re
                                        16, 0, 0);
     }
   };
+  (void)fetch_stage; (void)store_stage; (void)issue_stage;
 
   v16i acc[FN][FM];
 #pragma unroll
@@ -162,37 +193,53 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(const uint8_t* __re
   const int h = lane >> 5;
   const int nk = (int)(K / (2 * kRowBytes));
 
+  if constexpr (QV_DMA) {
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue_stage(s, (int64_t)s * kRowBytes);
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) issue_stage(s, (int64_t)s * kRowBytes);
+  } else {
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) {
+        fetch_stage((int64_t)s * kRowBytes);
+        store_stage(s);
+      }
+  }
 
   for (int kt = 0; kt < nk; ++kt) {
-    // Stage kt has landed once at most STAGES - 2 later stages are still in flight.
-    if (kt + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * kLoads>();
-    else wait_vmcnt<0>();
+    if constexpr (QV_DMA) {
+      // Stage kt has landed once at most STAGES - 2 later stages are still in flight.
+      if (kt + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * kLoads>();
+      else wait_vmcnt<0>();
+    }
     __syncthreads();  // every wave's share of stage kt is in LDS; stage kt - 1 is consumed
-    if (kt + STAGES - 1 < nk) issue_stage((kt + STAGES - 1) % STAGES, (int64_t)(kt + STAGES - 1) * kRowBytes);
+    const bool refill = kt + STAGES - 1 < nk;
+    if constexpr (QV_DMA) {
+      if (refill) issue_stage((kt + STAGES - 1) % STAGES, (int64_t)(kt + STAGES - 1) * kRowBytes);
+    } else {
+      if (refill) fetch_stage((int64_t)(kt + STAGES - 1) * kRowBytes);
+    }
 
     const uint8_t* As = lds + (kt % STAGES) * kStageBytes;
     const uint8_t* Bs = As + BN * kRowBytes;
-    u32x4 pa[FN][2], pb[FM][2];
+    u32x4 pa[FN][kReads], pb[FM][kReads];
 #pragma unroll
     for (int a = 0; a < FN; ++a) {
       const int r = wn * WN + 32 * a + r32;
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-        pa[a][q] = *reinterpret_cast<const u32x4*>(As + r * kRowBytes + 16 * ((2 * q + h) ^ swz(r)));
+      for (int q = 0; q < kReads; ++q)
+        pa[a][q] = *reinterpret_cast<const u32x4*>(As + r * kRowBytes + 16 * ((2 * q + h) ^ swz<U>(r)));
     }
 #pragma unroll
     for (int c = 0; c < FM; ++c) {
       const int r = wm * WM + 32 * c + r32;
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-        pb[c][q] = *reinterpret_cast<const u32x4*>(Bs + r * kRowBytes + 16 * ((2 * q + h) ^ swz(r)));
+      for (int q = 0; q < kReads; ++q)
+        pb[c][q] = *reinterpret_cast<const u32x4*>(Bs + r * kRowBytes + 16 * ((2 * q + h) ^ swz<U>(r)));
     }
-    // Four K32 sub-steps: sub-step s uses dwords 2(s&1), 2(s&1)+1 of read q = s >> 1.
+    // K32 sub-steps: sub-step s uses dwords 2(s&1), 2(s&1)+1 of read q = s >> 1.
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < kSub; ++s) {
       v4i fa[FN];
 #pragma unroll
       for (int a = 0; a < FN; ++a) {
@@ -209,14 +256,19 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(const uint8_t* __re
     }
     // Schedule: the fragment reads, the first sub-step's widening, then one MFMA per three VALU
     // ops so the remaining widening overlaps the matrix core.
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * (FN + FM), 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads * (FN + FM), 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 6 * (FN + FM), 0);
 #pragma unroll
-    for (int i = 0; i < 6 * (FN + FM); ++i) {
+    for (int i = 0; i < 2 * (kSub - 1) * (FN + FM); ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * FN * FM, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kSub * FN * FM - 2 * (kSub - 1) * (FN + FM), 0);
+    if constexpr (!QV_DMA) {
+      // The buffer of stage kt + STAGES - 1 held stage kt - 1, which every wave finished reading
+      // before this iteration's barrier.
+      if (refill) store_stage((kt + STAGES - 1) % STAGES);
+    }
   }
 
   // Epilogue.  The lane holds, for fragment (a, c) and register group vg, outputs
@@ -283,30 +335,47 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(const uint8_t* __re
   }
 }
 
-template <int BN, int BM, int STAGES, bool kBF16Out, bool kGelu>
+template <int BN, int BM, int RB, int STAGES, bool kBF16Out, bool kGelu>
 hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
                     int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
-  constexpr size_t kStageLds = (size_t)STAGES * (BN + BM) * kRowBytes;
+  constexpr size_t kStageLds = (size_t)STAGES * (BN + BM) * RB;
   constexpr size_t kOutLds = 4 * (size_t)(BM / 2) * ((BN / 2) * (kBF16Out ? 2 : 4) + (kBF16Out ? 8 : 16));
   constexpr size_t kLds = kStageLds > kOutLds ? kStageLds : kOutLds;
   static int attr_set[16] = {0};  // per device: allow more than 64 KB of dynamic LDS once
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
   if (!attr_set[dev]) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a4_gemm_kernel<BN, BM, STAGES, kBF16Out, kGelu>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a4_gemm_kernel<BN, BM, RB, STAGES, kBF16Out, kGelu>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
     if (e != hipSuccess) return e;
     attr_set[dev] = 1;
   }
   const int64_t blocks = (N / BN) * ((M + BM - 1) / BM);
-  hipLaunchKernelGGL((w4a4_gemm_kernel<BN, BM, STAGES, kBF16Out, kGelu>), dim3((unsigned)blocks), dim3(kThreads), kLds,
+  hipLaunchKernelGGL((w4a4_gemm_kernel<BN, BM, RB, STAGES, kBF16Out, kGelu>), dim3((unsigned)blocks), dim3(kThreads), kLds,
                      st, Xq, xs, Wq, ws, bias, M, N, K, Y, ldy);
   return hipGetLastError();
 }
 
 // 128 x 128 tiles (64 x 64 per wave): about 160 registers per lane and 48 KB of LDS, so three
 // blocks share a CU and one block's barrier, prologue and epilogue overlap another's MFMAs.
-constexpr int kTileN = 128, kTileM = 128;
+#ifndef QV_TILE_N
+#define QV_TILE_N 128
+#define QV_TILE_M 128
+#endif
+constexpr int kTileN = QV_TILE_N, kTileM = QV_TILE_M;
+
+
+template <bool kBF16Out, bool kGelu>
+hipError_t launch_k(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
+                    int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
+  // 128 codes (64 bytes of every row) per stage; a 256-code stage variant is kept selectable for
+  // measurements (it halves the barriers but its 64 KB ring leaves two blocks per CU).
+  if constexpr (QV_RB128) {
+    if ((K % 256) == 0)
+      return launch_t<kTileN, kTileM, 128, QV_STAGES_128, kBF16Out, kGelu>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+  }
+  return launch_t<kTileN, kTileM, 64, QV_STAGES, kBF16Out, kGelu>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+}
 
 }  // namespace
 
@@ -314,11 +383,11 @@ hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* xs, const uint8_t* W
                             const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out,
                             int64_t ldy, hipStream_t st) {
   if (bf16_out) {
-    return gelu ? launch_t<kTileN, kTileM, QV_STAGES, true, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
-                : launch_t<kTileN, kTileM, QV_STAGES, true, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+    return gelu ? launch_k<true, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
+                : launch_k<true, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
   }
-  return gelu ? launch_t<kTileN, kTileM, QV_STAGES, false, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
-              : launch_t<kTileN, kTileM, QV_STAGES, false, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+  return gelu ? launch_k<false, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
+              : launch_k<false, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
 }
 
 }  // namespace qv
