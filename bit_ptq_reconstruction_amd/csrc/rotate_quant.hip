@@ -28,6 +28,10 @@ namespace {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+#ifndef QV_RQ_PREFETCH
+#define QV_RQ_PREFETCH 0  // 1: keep the next row group's raw data in registers (3 waves/SIMD instead of 4)
+#endif
+
 constexpr int kThreads = 256;
 constexpr float kMagic = 12582920.0f;  // 1.5 * 2^23 + 8: its low mantissa byte holds rne(t) + 8
 
@@ -136,8 +140,10 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const In* __rest
     const int64_t r = grp * L::kRowsPerWave + sub;
     return r < M ? r : M - 1;
   };
+#if QV_RQ_PREFETCH
   RawRow<In> next;
   if (g < groups) load_raw<K, In>(X + row_of(g) * ldx, lane, next);
+#endif
 
   fill_multiplier_table<K>(mult, cm_lds);
   __syncthreads();
@@ -145,9 +151,13 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const In* __rest
   for (; g < groups; g += wave_stride) {
     const int64_t row = g * L::kRowsPerWave + sub;
     float v[8][8];
+#if QV_RQ_PREFETCH
     unpack_raw<In>(next, v);
     // Prefetch the next row group while this one is transformed.
     if (g + wave_stride < groups) load_raw<K, In>(X + row_of(g + wave_stride) * ldx, lane, next);
+#else
+    load_row<K, In>(X + row_of(g) * ldx, lane, v);
+#endif
 
     fwht_row_regs<K>(v, lane);
 
