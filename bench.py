@@ -75,6 +75,7 @@ def main():
 
     import bit_ptq_reconstruction_amd as qv
     from bit_ptq_reconstruction_amd import synth
+    from bit_ptq_reconstruction_amd import workload
     from bit_ptq_reconstruction_amd.configs import EPI_GELU, WORKLOADS
 
     wl = WORKLOADS[args.workload]
@@ -85,32 +86,9 @@ def main():
     stream = torch.cuda.current_stream()
 
     # ---------------------------------------------------------------- resident inputs and weights
-    layers = []
-    for blk in range(wl.blocks):
-        for li, lin in enumerate(wl.linears):
-            x_seed = lin.x_seed + (1000 * blk if wl.blocks > 1 else 0)
-            w_seed = lin.w_seed + (1000 * blk if wl.blocks > 1 else 0)
-            chained = wl.chain_mlp and li > 0
-            in_dt = torch.bfloat16 if wl.in_dtype == "bf16" else torch.float32
-            X = None if chained else synth.vggt_activations_torch(M, lin.K, x_seed, in_dt, dev)
-            W = synth.weights_torch(lin.N, lin.K, w_seed, dev)
-            s = torch.empty(lin.K, device=dev)
-            inv = torch.empty(lin.K, device=dev)
-            calib = X if X is not None else synth.vggt_activations_torch(synth.FRAME_TOKENS, lin.K, x_seed, in_dt, dev)
-            qv.qv_smooth_calibrate(calib[:synth.FRAME_TOKENS], W, s, inv, 0.5)
-            Wq = torch.empty((lin.N, lin.K // 2), dtype=torch.uint8, device=dev)
-            ws = torch.empty((lin.N,), dtype=torch.float32, device=dev)
-            qv.qv_pack_weights(W, s, Wq, ws)
-            del W
-            out_dt = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
-            layers.append(dict(lin=lin, X=X, inv=inv, Wq=Wq, ws=ws,
-                               Xq=torch.empty((M, lin.K // 2), dtype=torch.uint8, device=dev),
-                               xs=torch.empty((M,), dtype=torch.float32, device=dev),
-                               Y=torch.empty((M, lin.N), dtype=out_dt, device=dev)))
-    if wl.chain_mlp:
-        for i in range(1, len(layers)):
-            layers[i]["X"] = layers[i - 1]["Y"]
-    torch.cuda.synchronize()
+    # A multi-block stack shares the per-shape code/scale/output buffers across blocks (each step
+    # overwrites them in order); activations and packed weights are per layer.
+    layers = workload.build(qv, wl, dev, share_outputs=wl.blocks > 1)
 
     if args.copy_probe_mib > 0:
         nbytes = args.copy_probe_mib << 20
@@ -128,10 +106,10 @@ def main():
             if record:
                 e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
                 e[0].record(stream)
-            qv.qv_hadamard_smooth_quant(L["X"], L["inv"], L["Xq"], L["xs"], stream)
+            qv.qv_hadamard_smooth_quant(L.X, L.inv, L.Xq, L.xs, stream)
             if record:
                 e[1].record(stream)
-            qv.qv_w4a4_gemm(L["Xq"], L["xs"], L["Wq"], L["ws"], None, L["Y"], L["lin"].epi, stream)
+            qv.qv_w4a4_gemm(L.Xq, L.xs, L.Wq, L.ws, None, L.Y, L.lin.epi, stream)
             if record:
                 e[2].record(stream)
                 events.append((L, e))
@@ -146,34 +124,45 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
 
-    ops_per_step = sum(2.0 * M * L["lin"].N * L["lin"].K for L in layers)
+    ops_per_step = sum(2.0 * M * L.lin.N * L.lin.K for L in layers)
     value = ops_per_step / (wall / args.steps) / 1e12
 
     # ---------------------------------------------------------------- per-kernel times (HIP events)
     k1_t, k2_t, k1_bytes, k2_ops = 0.0, 0.0, 0.0, 0.0
     per_layer = {}
     for L, e in events:
-        lin = L["lin"]
+        lin = L.lin
         t1 = e[0].elapsed_time(e[1]) * 1e-3
         t2 = e[1].elapsed_time(e[2]) * 1e-3
-        in_b = L["X"].element_size()
+        in_b = L.X.element_size()
         b1 = M * lin.K * in_b + M * (lin.K // 2) + 4 * M
         o2 = 2.0 * M * lin.N * lin.K
         k1_t += t1
         k2_t += t2
         k1_bytes += b1
         k2_ops += o2
-        d = per_layer.setdefault(lin.name, dict(n=0, k1=0.0, k2=0.0, b1=b1, o2=o2, K=lin.K, N=lin.N))
+        d = per_layer.setdefault(lin.name, dict(n=0, k1=0.0, k2=0.0, b1=b1, o2=o2, K=lin.K, N=lin.N,
+                                                t1s=[], t2s=[]))
         d["n"] += 1
         d["k1"] += t1
         d["k2"] += t2
+        d["t1s"].append(t1)
+        d["t2s"].append(t2)
     n_launch = len(events)
     k2_tops = k2_ops / k2_t / 1e12
     k1_gbps = k1_bytes / k1_t / 1e9
+    def pct(ts):
+        q = np.percentile(np.asarray(ts) * 1e6, [10, 50, 90])
+        return [round(float(v), 2) for v in q]
+
     kernels = {name: {"K": d["K"], "N": d["N"], "rotate_quant_us": 1e6 * d["k1"] / d["n"],
+                      "rotate_quant_us_p10_p50_p90": pct(d["t1s"]),
                       "rotate_quant_GBps": d["b1"] * d["n"] / d["k1"] / 1e9,
-                      "gemm_us": 1e6 * d["k2"] / d["n"], "gemm_TOPS": d["o2"] * d["n"] / d["k2"] / 1e12}
+                      "gemm_us": 1e6 * d["k2"] / d["n"], "gemm_us_p10_p50_p90": pct(d["t2s"]),
+                      "gemm_TOPS": d["o2"] * d["n"] / d["k2"] / 1e12}
                for name, d in per_layer.items()}
+    wq_bytes = sum(L.Wq.numel() + 4 * L.ws.numel() for L in layers)
+    bf16_w_bytes = sum(2 * L.lin.N * L.lin.K for L in layers)
 
     gemm_hash = kernel_source_hash(["w4a4_gemm.hip"])
     rq_hash = kernel_source_hash(["rotate_quant.hip", "fwht_regs.h"])
@@ -196,6 +185,8 @@ def main():
                                   "bytes_per_launch": k1_bytes / n_launch},
         "kernels": kernels,
         "rotate_quant_share_of_linear_time": round(k1_t / (k1_t + k2_t), 4),
+        "weights_resident": {"int4_bytes_with_scales": wq_bytes, "bf16_bytes": bf16_w_bytes,
+                             "ratio": round(bf16_w_bytes / wq_bytes, 3)},
         "gemm_only_TOPS": round(k2_tops, 2),
         "source_hash": {"w4a4_gemm": gemm_hash, "rotate_quant": rq_hash},
     }
@@ -204,7 +195,7 @@ def main():
     if not args.no_bf16_baseline:
         base = []
         for L in layers[:len(wl.linears)]:
-            lin = L["lin"]
+            lin = L.lin
             Xb = synth.vggt_activations_torch(M, lin.K, 0, torch.bfloat16, dev)
             Wb = synth.weights_torch(lin.N, lin.K, 1, dev).to(torch.bfloat16)
             base.append((Xb, Wb, lin.epi))

@@ -1,0 +1,116 @@
+"""Device-resident state of a named workload and the two library calls of one online linear.
+
+A layer holds what the online step reads and writes: its input activations X (bf16 or fp32
+[M][K]), the activation-side smoothing multipliers 1/s ([K] fp32), the packed int4 weights and
+their per-channel scales (prepared once, offline), the code/scale buffers of the quantized
+activations and the output Y [M][N].  ``run_linear`` is the online path: rotate-smooth-quantize,
+then the int4 GEMM with its dequant (+GELU) epilogue, both on the given stream.
+
+Smoothing follows the method's calibration reading: the factors of a layer come from the first
+frame (1374 rows) of that layer's own input activations and from its weights.  In the MLP chain
+fc2's input is fc1's output, so fc2 is calibrated on fc1's output for frame 0.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from . import synth
+from .configs import Linear, Workload
+
+
+@dataclass
+class Layer:
+    lin: Linear
+    block: int
+    X: object      # [M][K] activations (None until a chain links it)
+    inv: object    # [K] fp32, 1 / smoothing factor
+    Wq: object     # [N][K/2] uint8 packed int4 weights
+    ws: object     # [N] fp32 weight scales
+    Xq: object     # [M][K/2] uint8 packed int4 activation codes
+    xs: object     # [M] fp32 activation scales
+    Y: object      # [M][N] output
+
+
+def torch_dtype(name: str):
+    import torch
+
+    return {"bf16": torch.bfloat16, "fp32": torch.float32}[name]
+
+
+def seeds(wl: Workload, lin: Linear, block: int):
+    """(activation seed, weight seed) of a linear in a given block."""
+    if wl.blocks > 1:
+        return lin.x_seed + 1000 * block, lin.w_seed + 1000 * block
+    return lin.x_seed, lin.w_seed
+
+
+def run_linear(qv, L: Layer, stream=None) -> None:
+    """The online W4A4 linear: qv_hadamard_smooth_quant, then qv_w4a4_gemm."""
+    qv.qv_hadamard_smooth_quant(L.X, L.inv, L.Xq, L.xs, stream)
+    qv.qv_w4a4_gemm(L.Xq, L.xs, L.Wq, L.ws, None, L.Y, L.lin.epi, stream)
+
+
+def build(qv, wl: Workload, device, share_outputs: bool = False):
+    """Allocate and prepare every layer of ``wl`` on ``device`` (timing inputs, seeded on device).
+
+    Activations are drawn per layer and per block.  With ``share_outputs`` the code/scale buffers
+    and outputs are shared by the layers of equal shape across blocks (a 48-block stack would
+    otherwise hold 48 copies of buffers that each step overwrites in order).  Weights are packed
+    with ``qv_pack_weights`` after ``qv_smooth_calibrate`` on frame 0 of the layer's input.
+    """
+    import torch
+
+    M = wl.M
+    in_dt, out_dt = torch_dtype(wl.in_dtype), torch_dtype(wl.out_dtype)
+    shared = {}
+
+    def buffers(lin):
+        key = (lin.name, lin.K, lin.N)
+        if share_outputs and key in shared:
+            return shared[key]
+        b = (torch.empty((M, lin.K // 2), dtype=torch.uint8, device=device),
+             torch.empty((M,), dtype=torch.float32, device=device),
+             torch.empty((M, lin.N), dtype=out_dt, device=device))
+        shared[key] = b
+        return b
+
+    layers = []
+    for blk in range(wl.blocks):
+        prev = None
+        for li, lin in enumerate(wl.linears):
+            x_seed, w_seed = seeds(wl, lin, blk)
+            chained = wl.chain_mlp and li > 0
+            X = None if chained else synth.vggt_activations_torch(M, lin.K, x_seed, in_dt, device)
+            W = synth.weights_torch(lin.N, lin.K, w_seed, device)
+            s = torch.empty(lin.K, device=device)
+            inv = torch.empty(lin.K, device=device)
+            if chained:
+                calib = frame0_output(qv, prev, device)
+            else:
+                calib = X[:synth.FRAME_TOKENS]
+            qv.qv_smooth_calibrate(calib, W, s, inv, 0.5)
+            Wq = torch.empty((lin.N, lin.K // 2), dtype=torch.uint8, device=device)
+            ws = torch.empty((lin.N,), dtype=torch.float32, device=device)
+            qv.qv_pack_weights(W, s, Wq, ws)
+            del W
+            Xq, xs, Y = buffers(lin)
+            L = Layer(lin, blk, X, inv, Wq, ws, Xq, xs, Y)
+            if chained:
+                L.X = prev.Y
+            layers.append(L)
+            prev = L
+    torch.cuda.synchronize(device)
+    return layers
+
+
+def frame0_output(qv, L: Layer, device):
+    """Output of layer ``L`` on the first frame of its input (calibration rows of the next layer)."""
+    import torch
+
+    F = min(synth.FRAME_TOKENS, L.X.shape[0])
+    tmp = Layer(L.lin, L.block, L.X[:F], L.inv, L.Wq, L.ws,
+                torch.empty((F, L.lin.K // 2), dtype=torch.uint8, device=device),
+                torch.empty((F,), dtype=torch.float32, device=device),
+                torch.empty((F, L.lin.N), dtype=L.Y.dtype, device=device))
+    run_linear(qv, tmp)
+    return tmp.Y

@@ -31,8 +31,12 @@ CODE_MISMATCH_MAX = 1e-4
 OUT_REL_MAX = 1e-3
 
 
-def code_bounds(X, mult, Xhat=None):
-    """Exact code-space values t and the per-element tolerance tau for rows X (fp32 values)."""
+def code_bounds(X, mult, Xhat=None, dX=None):
+    """Exact code-space values t and the per-element tolerance tau for rows X (fp32 values).
+
+    ``dX`` (optional, same shape) bounds how far the GPU's input rows may differ from X elementwise
+    (a chained layer fed the GPU's previous output): each rotated element then moves by at most
+    sum_i |dX_i| / sqrt(K) more, since every entry of H / sqrt(K) is +-1/sqrt(K)."""
     X = np.asarray(X, dtype=np.float64)
     M, K = X.shape
     if Xhat is None:
@@ -48,6 +52,9 @@ def code_bounds(X, mult, Xhat=None):
     with np.errstate(divide="ignore", invalid="ignore"):
         t = np.where(s[:, None] > 0, xt / s[:, None], 0.0)
         e_x = L * U * np.sum(np.abs(X), axis=1) / math.sqrt(K)  # butterfly error bound per row
+        if dX is not None:
+            d1 = np.sum(np.abs(np.asarray(dX, dtype=np.float64)), axis=1) / math.sqrt(K)
+            e_x = e_x + L * U * d1 + d1
         rel_scale = np.where(a > 0, e_x * np.max(np.abs(m)) / a, 0.0) + 4 * U
         tau = 2.0 * ((e_x[:, None] * np.abs(m)[None, :] + 2 * U * np.abs(xt)) / np.where(s > 0, s, 1.0)[:, None]
                      + np.abs(t) * rel_scale[:, None])
@@ -88,6 +95,7 @@ def bf16_round(y):
 
 
 def check_outputs(y_gpu, y_ref, out_bf16: bool, label=""):
+    """Returns the worst relative error (fp32 outputs) or the worst difference in bf16 ulps."""
     y_gpu = np.asarray(y_gpu, dtype=np.float64)
     y_ref = np.asarray(y_ref, dtype=np.float64)
     if out_bf16:
@@ -96,7 +104,10 @@ def check_outputs(y_gpu, y_ref, out_bf16: bool, label=""):
         bad = np.abs(y_gpu - r) > ulp + 1e-38
         assert not np.any(bad), (f"{label}: {int(bad.sum())} bf16 outputs beyond 1 ulp, e.g. "
                                  f"{[(float(y_gpu[tuple(i)]), float(y_ref[tuple(i)])) for i in np.argwhere(bad)[:3]]}")
-        return float(np.max(np.abs(y_gpu - y_ref) / np.maximum(np.abs(y_ref), 1e-300))) if y_ref.size else 0.0
+        # Reported: the largest difference from the rounded reference, in bf16 ulps at its magnitude.
+        with np.errstate(divide="ignore", invalid="ignore"):
+            ulps = np.where(np.abs(y_gpu - r) > 0, np.abs(y_gpu - r) / np.maximum(ulp, 1e-38), 0.0)
+        return float(np.max(ulps)) if y_ref.size else 0.0
     with np.errstate(divide="ignore", invalid="ignore"):
         rel = np.abs(y_gpu - y_ref) / np.abs(y_ref)
     rel[(y_gpu == y_ref)] = 0.0

@@ -1,0 +1,179 @@
+"""Parity at the workloads' full sizes, in the launch configuration the benchmark times.
+
+Every linear of each workload runs through the same two C-ABI calls and the same shapes as the
+benchmark step (``workload.run_linear``) on device-generated VGGT-shaped activations.  The oracle
+cannot redo a whole workload, so it checks:
+  * every packed weight code and weight scale (the offline step, all N x K codes);
+  * a sample of token rows: special-token rows of the first frame, rows of the last frame's ragged
+    tile, and seeded random rows -- their codes and scales, and every output column of those rows.
+Expected values come from the oracle on the same inputs; where a code differs it must be an
+admissible near-tie (tests/acceptance.py), and the output reference then takes that code.
+
+The MLP chain (fc1 -> GELU -> bf16 -> fc2 at width 4096) is checked two ways:
+  * stage-wise: the rotate-quantize step at width 4096 is fed the oracle's own fc1 output rows;
+  * end to end: the GPU chain's fc2 codes are compared with the oracle's chain, with the code
+    bound widened by how far the GPU's fc1 output may move fc2's rotated input (each rotated
+    element moves by at most sum_i |dX_i| / sqrt(K), the rotation being orthonormal with entries
+    +-1/sqrt(K)).
+Sources: page "十亿参数的三维重建模型，能塞进手机吗？" (gslzct.com), 训练后量化（PTQ）,
+预全局旋转 and 后局部平滑.
+"""
+import numpy as np
+import pytest
+
+import acceptance as acc
+import oracle
+from bit_ptq_reconstruction_amd import configs, synth, workload
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+SAMPLE_RANDOM = 192
+
+
+@pytest.fixture(scope="module")
+def qv():
+    import bit_ptq_reconstruction_amd as m
+
+    m.lib()
+    return m
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def sample_rows(M, seed):
+    """First-frame special and patch rows, the last 40 rows (ragged M tile), seeded random rows."""
+    rng = np.random.default_rng([seed, 0x5A])
+    rows = set(range(0, min(12, M))) | set(range(max(0, M - 40), M))
+    rows |= set(rng.choice(M, size=min(SAMPLE_RANDOM, M), replace=False).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def host(t):
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def oracle_smoothing(X0, W):
+    Xh = oracle.rotate(X0, oracle.ROT_FWHT)
+    Wh = oracle.rotate(W, oracle.ROT_FWHT)
+    return oracle.smoothing(Xh, Wh, 0.5)
+
+
+def prepare_layer(qv, dev, lin, M, X, W_host, calib_host, out_dtype):
+    """Pack weights with oracle smoothing factors (calibrated on ``calib_host``); allocate buffers."""
+    s, inv = oracle_smoothing(calib_host, W_host)
+    Wq = torch.empty((lin.N, lin.K // 2), dtype=torch.uint8, device=dev)
+    ws = torch.empty((lin.N,), dtype=torch.float32, device=dev)
+    qv.qv_pack_weights(torch.from_numpy(W_host).to(dev), torch.from_numpy(s).to(dev), Wq, ws)
+    L = workload.Layer(lin, 0, X, torch.from_numpy(inv).to(dev), Wq, ws,
+                       torch.empty((M, lin.K // 2), dtype=torch.uint8, device=dev),
+                       torch.empty((M,), dtype=torch.float32, device=dev),
+                       torch.empty((M, lin.N), dtype=workload.torch_dtype(out_dtype), device=dev))
+    return L, s, inv
+
+
+def check_weights(L, W_host, s, label):
+    """All weight codes and scales against the oracle's offline step."""
+    Wq_g, ws_g = L.Wq.cpu().numpy(), L.ws.cpu().numpy()
+    Wh = oracle.rotate(W_host, oracle.ROT_FWHT)
+    q_ref, s_ref = oracle.quantize_rows(Wh, s)
+    t, tau, _, rel = acc.code_bounds(W_host, s, Wh)
+    q_gpu = oracle.unpack_int4(Wq_g)
+    rate = acc.check_codes(q_gpu, q_ref, t, tau, f"{label} weights")
+    acc.check_scales(ws_g, s_ref, rel, f"{label} weights")
+    return np.where(q_gpu != q_ref, q_gpu, q_ref), s_ref, rate
+
+
+def check_rows(L, rows, X_rows, inv, Wcodes, ws_ref, label, dX=None):
+    """Codes and scales of the sampled rows, then every output column of those rows."""
+    Xq_g = L.Xq[torch.from_numpy(rows).to(L.Xq.device)].cpu().numpy()
+    xs_g = L.xs[torch.from_numpy(rows).to(L.xs.device)].cpu().numpy()
+    Y_g = host(L.Y[torch.from_numpy(rows).to(L.Y.device)])
+    Xh = oracle.rotate(X_rows, oracle.ROT_FWHT)
+    q_ref, s_ref = oracle.quantize_rows(Xh, inv)
+    t, tau, _, rel = acc.code_bounds(X_rows, inv, Xh, dX=dX)
+    q_gpu = oracle.unpack_int4(Xq_g)
+    rate = acc.check_codes(q_gpu, q_ref, t, tau, f"{label} activations")
+    acc.check_scales(xs_g, s_ref, rel, f"{label} activations")
+    codes = np.where(q_gpu != q_ref, q_gpu, q_ref)
+    Y_ref = oracle.w4a4_gemm(oracle.pack_int4(codes), s_ref, oracle.pack_int4(Wcodes), ws_ref, None, L.lin.epi)
+    worst = acc.check_outputs(Y_g, Y_ref, L.Y.dtype == torch.bfloat16, f"{label} outputs")
+    return rate, worst, Y_ref
+
+
+def full_size_linear(qv, dev, wl, lin, M, x_seed, w_seed):
+    in_dt = workload.torch_dtype(wl.in_dtype)
+    X = synth.vggt_activations_torch(M, lin.K, x_seed, in_dt, dev)
+    W_host = synth.weights(lin.N, lin.K, w_seed)
+    X0 = host(X[:synth.FRAME_TOKENS])
+    L, s, inv = prepare_layer(qv, dev, lin, M, X, W_host, X0, wl.out_dtype)
+    workload.run_linear(qv, L)
+    torch.cuda.synchronize()
+    label = f"{wl.name}/{lin.name} M={M} K={lin.K} N={lin.N}"
+    Wcodes, ws_ref, wrate = check_weights(L, W_host, s, label)
+    rows = sample_rows(M, x_seed)
+    X_rows = host(X[torch.from_numpy(rows).to(dev)])
+    rate, worst, _ = check_rows(L, rows, X_rows, inv, Wcodes, ws_ref, label)
+    print(f"{label}: weight mismatch {wrate:.1e}, row mismatch {rate:.1e} over {len(rows)} rows, "
+          f"worst output error {worst:.2e} ({'bf16 ulps' if wl.out_dtype == 'bf16' else 'relative'})", flush=True)
+    del L, X
+
+
+@pytest.mark.parametrize("name", ["qkv_8frames", "block_32frames", "stack48_100frames"])
+def test_full_size_linears(qv, dev, name):
+    wl = configs.WORKLOADS[name]
+    for lin in wl.linears:
+        x_seed, w_seed = workload.seeds(wl, lin, 0)
+        full_size_linear(qv, dev, wl, lin, wl.M, x_seed, w_seed)
+        torch.cuda.empty_cache()
+
+
+def test_full_size_mlp_chain(qv, dev):
+    wl = configs.WORKLOADS["mlp_24frames"]
+    fc1, fc2 = wl.linears
+    M = wl.M
+    in_dt = workload.torch_dtype(wl.in_dtype)
+    X = synth.vggt_activations_torch(M, fc1.K, fc1.x_seed, in_dt, dev)
+    W1, W2 = synth.weights(fc1.N, fc1.K, fc1.w_seed), synth.weights(fc2.N, fc2.K, fc2.w_seed)
+    X0 = host(X[:synth.FRAME_TOKENS])
+    L1, s1, inv1 = prepare_layer(qv, dev, fc1, M, X, W1, X0, wl.out_dtype)
+    Wc1, ws1, _ = check_weights(L1, W1, s1, "mlp/fc1")
+
+    # fc2 is calibrated on the oracle's fc1 output for frame 0 (bf16, as the chain stores it).
+    q0, xs0 = oracle.hadamard_smooth_quant(X0, inv1, oracle.ROT_FWHT)
+    Wq1_o, ws1_o = oracle.pack_weights(W1, s1, oracle.ROT_FWHT)
+    Y1_0 = synth.round_to_bf16(oracle.w4a4_gemm(q0, xs0, Wq1_o, ws1_o, None, fc1.epi))
+    L2, s2, inv2 = prepare_layer(qv, dev, fc2, M, L1.Y, W2, Y1_0, wl.out_dtype)
+    Wc2, ws2, _ = check_weights(L2, W2, s2, "mlp/fc2")
+
+    workload.run_linear(qv, L1)
+    workload.run_linear(qv, L2)
+    torch.cuda.synchronize()
+
+    rows = sample_rows(M, 7)
+    X_rows = host(X[torch.from_numpy(rows).to(dev)])
+    r1, w1, Y1_ref = check_rows(L1, rows, X_rows, inv1, Wc1, ws1, "mlp/fc1")
+    Y1_ref = synth.round_to_bf16(Y1_ref)
+    Y1_gpu = host(L1.Y[torch.from_numpy(rows).to(dev)])
+    dX = np.abs(Y1_gpu.astype(np.float64) - Y1_ref)
+    r2, w2, _ = check_rows(L2, rows, Y1_ref, inv2, Wc2, ws2, "mlp/fc2 (chain)", dX=dX)
+    print(f"mlp chain: fc1 row mismatch {r1:.1e} (out {w1:.2e}); fc1 outputs differing from the oracle "
+          f"{np.mean(dX > 0):.2e}; fc2 row mismatch {r2:.1e} (out {w2:.2e})", flush=True)
+
+    # Stage-wise: the width-4096 rotate-quantize fed the oracle's own fc1 output rows.
+    Xs = torch.from_numpy(Y1_ref.astype(np.float32)).to(dev).to(torch.bfloat16)
+    Xq = torch.empty((len(rows), fc2.K // 2), dtype=torch.uint8, device=dev)
+    xs = torch.empty((len(rows),), dtype=torch.float32, device=dev)
+    qv.qv_hadamard_smooth_quant(Xs, L2.inv, Xq, xs)
+    torch.cuda.synchronize()
+    Xh = oracle.rotate(Y1_ref, oracle.ROT_FWHT)
+    q_ref, s_ref = oracle.quantize_rows(Xh, inv2)
+    t, tau, _, rel = acc.code_bounds(Y1_ref, inv2, Xh)
+    rate = acc.check_codes(oracle.unpack_int4(Xq.cpu().numpy()), q_ref, t, tau, "mlp/fc2 stage-wise")
+    acc.check_scales(xs.cpu().numpy(), s_ref, rel, "mlp/fc2 stage-wise")
+    print(f"mlp fc2 stage-wise mismatch {rate:.1e}", flush=True)

@@ -65,7 +65,8 @@ def check_quant_against_oracle(X, mult, q_packed, s_gpu, mode, label):
     q_gpu = oracle.unpack_int4(q_packed)
     rate = acc.check_codes(q_gpu, q_ref, t, tau, label)
     acc.check_scales(s_gpu, s_ref, rel_scale, label)
-    return rate, q_gpu
+    # The oracle's codes, with the GPU's admissible near-tie codes where the two differ.
+    return rate, np.where(q_gpu != q_ref, q_gpu, q_ref), s_ref
 
 
 # ---------------------------------------------------------------------------- rotate-quantize
@@ -80,7 +81,7 @@ def test_hadamard_smooth_quant_parity(qv, dev, K, dtype, M, smooth, pad):
     W = synth.weights(128, K, seed=3)
     mult = smoothing_for(X, W)[1] if smooth else None
     q, s = run_quant(qv, dev, X, dtype, mult, ld_pad=pad)
-    rate, _ = check_quant_against_oracle(X, mult, q, s, oracle.ROT_EXPLICIT, f"K={K} {dtype} M={M}")
+    rate, _, _ = check_quant_against_oracle(X, mult, q, s, oracle.ROT_EXPLICIT, f"K={K} {dtype} M={M}")
     print(f"K={K} {dtype} M={M}: code mismatch rate {rate:.2e}")
 
 
@@ -240,9 +241,11 @@ def test_linear_against_oracle_end_to_end(qv, dev):
     Y = torch.empty((M, N), dtype=torch.float32, device=dev)
     qv.qv_w4a4_gemm(Xq, xs, Wq, ws, None, Y)
     torch.cuda.synchronize()
-    check_quant_against_oracle(W, s, Wq.cpu().numpy(), ws.cpu().numpy(), oracle.ROT_EXPLICIT, "weights")
-    check_quant_against_oracle(X, inv, Xq.cpu().numpy(), xs.cpu().numpy(), oracle.ROT_EXPLICIT, "activations")
-    Y_ref = oracle.w4a4_gemm(Xq.cpu().numpy(), xs.cpu().numpy(), Wq.cpu().numpy(), ws.cpu().numpy())
+    _, wc, ws_ref = check_quant_against_oracle(W, s, Wq.cpu().numpy(), ws.cpu().numpy(), oracle.ROT_EXPLICIT,
+                                               "weights")
+    _, xc, xs_ref = check_quant_against_oracle(X, inv, Xq.cpu().numpy(), xs.cpu().numpy(), oracle.ROT_EXPLICIT,
+                                               "activations")
+    Y_ref = oracle.w4a4_gemm(oracle.pack_int4(xc), xs_ref, oracle.pack_int4(wc), ws_ref)
     acc.check_outputs(Y.cpu().numpy(), Y_ref, False, "linear")
     # Quantization quality (reported): relative Frobenius error against the fp64 product, next to
     # the oracle's own W4A4 error on the same inputs (the two must agree closely).
