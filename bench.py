@@ -31,8 +31,9 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=50,
+                   help="untimed steps first: the GPU clock needs tens of milliseconds of load to ramp up from idle")
     p.add_argument("--workload", default="block_32frames")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
     p.add_argument("--no-bf16-baseline", action="store_true")

@@ -15,11 +15,13 @@
 //   * a fragment is two ds_read_b128 per lane (32 + 32 packed codes), feeding four MFMAs;
 //   * codes are widened to int8 with two masks: (p & 0xF0F0F0F0) keeps the odd-k nibbles as 16 q
 //     and ((p << 4) & 0xF0F0F0F0) the even-k ones.  Both operands carry the factor 16, so the
-//     accumulator holds 256 * acc (exact: |256 acc| <= 256 * 64 * 65536 < 2^31) and an arithmetic
-//     shift by 8 recovers acc.  A and B are widened the same way, so every k is paired with itself
-//     and the order of the terms inside a fragment does not matter;
+//     accumulator holds 256 * acc (exact: |256 acc| <= 256 * 64 * 65536 < 2^31); the epilogue
+//     folds the 2^-8 into the row scale.  A and B are widened the same way, so every k is paired
+//     with itself and the order of the terms inside a fragment does not matter;
 //   * the widening of the next operands is interleaved with the MFMAs (three VALU ops per MFMA), so
 //     the unpack runs on the vector ALU while the matrix core is busy.
+// The tile's row and column scales are fetched into LDS by LDS-DMA when the tile starts, so the
+// epilogue does not wait on global memory.
 // MFMA operand roles: A = weight tile (output rows i = n), B = activation tile (columns j = m): a
 // lane owns runs of four consecutive n of one m and writes each with one 8-byte (bf16) or 16-byte
 // (fp32) store.  Tiles are assigned XCD-major: the hardware deals blocks round-robin over the 8
@@ -81,30 +83,38 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// GELU(y) = y * Phi(y) with Phi(-|y|) = erfc(|y| / sqrt 2) / 2, erfc from the Chebyshev-fitted
-// approximation of Numerical Recipes (Press et al., "erfcc": fractional error below 1.2e-7 on the
-// whole real line).  In fp32 the largest relative error of this GELU is about 2.4e-5, down to the
-// smallest normal output.
+// GELU(y) = y Phi(y) = max(y, 0) - |y| Q(|y|), Q(x) = Phi(-x) = erfc(x / sqrt 2) / 2 (for y >= 0,
+// y Phi(y) = y - y Q(y); for y < 0 it is y Q(-y)).  Q is evaluated as t 2^(P(t) - x^2 log2(e) / 2)
+// with t = 1 / (1 + 0.35 x): the factor exp(-x^2/2) is exact in form, and P, a degree-5 polynomial
+// in t, carries log2 of the remaining slowly varying ratio.  The coefficients are a minimax fit of
+// log2(Q(x) / t) + x^2 log2(e) / 2 over x in [0, 13.5] (beyond that |y| Q(|y|) is below the fp32
+// normal range); in fp32 the largest relative error of the GELU is 1.4e-5 down to the smallest
+// normal output.  P's constant term carries +8, so 2^(...) stays normal wherever the output is;
+// the final 2^-8 undoes it.
 __device__ __forceinline__ float gelu(float y) {
-  const float z = fabsf(y) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
-  float p = 0.17087277f;
-  p = __builtin_fmaf(p, t, -0.82215223f);
-  p = __builtin_fmaf(p, t, 1.48851587f);
-  p = __builtin_fmaf(p, t, -1.13520398f);
-  p = __builtin_fmaf(p, t, 0.27886807f);
-  p = __builtin_fmaf(p, t, -0.18628806f);
-  p = __builtin_fmaf(p, t, 0.09678418f);
-  p = __builtin_fmaf(p, t, 0.37409196f);
-  p = __builtin_fmaf(p, t, 1.00002368f);
-  p = __builtin_fmaf(p, t, -1.26551223f);
-  // te = 2^24 erfc(z): the exponent carries a +24 so that exp(-z^2) stays a normal number wherever
-  // y * Phi(y) is one; the factor 2^-25 = 2^-24 / 2 is applied after the product with y.
-  const float te = t * __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fmaf(-z, z, p), 1.44269504088896341f, 24.0f));
-  return (y < 0.0f) ? (y * te) * 2.98023223876953125e-08f : y * __builtin_fmaf(te, -2.98023223876953125e-08f, 1.0f);
+  const float x = fabsf(y);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.35f, x, 1.0f));
+  float p = 0.3330344557762146f;
+  p = __builtin_fmaf(p, t, -1.0501084327697754f);
+  p = __builtin_fmaf(p, t, 0.7375118136405945f);
+  p = __builtin_fmaf(p, t, 0.3481525182723999f);
+  p = __builtin_fmaf(p, t, 1.47362220287323f);
+  p = __builtin_fmaf(p, t, 5.157796859741211f);
+  const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(x * -0.72134752044448170f, x, p));
+  return __builtin_fmaf((x * t) * e, -0.00390625f, fmaxf(y, 0.0f));
 }
 
-template <int BN, int BM, int RB, int STAGES, bool kBF16Out, bool kGelu>
+// LDS of a block: the stage ring (reused for output staging in the epilogue), then the tile's
+// BN weight scales and BM activation scales, fetched by LDS-DMA when the tile starts.
+template <int BN, int BM, int RB, int STAGES, bool kBF16Out>
+struct GemmLds {
+  static constexpr size_t kStage = (size_t)STAGES * (BN + BM) * RB;
+  static constexpr size_t kOut = 4 * (size_t)(BM / 2) * ((BN / 2) * (kBF16Out ? 2 : 4) + (kBF16Out ? 8 : 16));
+  static constexpr size_t kScaleOffset = kStage > kOut ? kStage : kOut;
+  static constexpr size_t kTotal = kScaleOffset + 4 * (size_t)(BN + BM);
+};
+
+template <int BN, int BM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 128 ? 2 : 3))) void w4a4_gemm_kernel(const uint8_t* __restrict__ Xq,
                                                             const float* __restrict__ x_scale,
                                                             const uint8_t* __restrict__ Wq,
@@ -123,6 +133,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
   constexpr int kStageBytes = (BN + BM) * kRowBytes;
   static_assert(kUnits % kThreads == 0, "tile must split evenly over the waves");
   static_assert(STAGES >= 2 && (STAGES - 2) * kLoads < 64, "pipeline depth");
+  static_assert((BN + BM) % 64 == 0, "whole waves of scale loads");
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
   const int tid = threadIdx.x;
@@ -193,6 +204,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
   const int h = lane >> 5;
   const int nk = (int)(K / (2 * kRowBytes));
 
+  // The tile's scales: scale slot i holds w_scale[n0 + i] (i < BN) or x_scale[m0 + i - BN] (rows
+  // past M repeat the last row); thread t fetches slots t, t + 256, ...  Issued before the stage
+  // loads, so the first iteration's vmcnt wait covers them.
+  float* const scales = reinterpret_cast<float*>(lds + GemmLds<BN, BM, RB, STAGES, kBF16Out>::kScaleOffset);
+#pragma unroll
+  for (int r = 0; r < (BN + BM + kThreads - 1) / kThreads; ++r) {
+    const int i = tid + kThreads * r;
+    if (kThreads * r + 64 * wave >= BN + BM) break;  // wave-uniform
+    const float* sp;
+    if (i < BN) {
+      sp = w_scale + n0 + i;
+    } else {
+      const int64_t mr = m0 + (i - BN);
+      sp = x_scale + (mr < M ? mr : M - 1);
+    }
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(sp),
+                                     reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                         reinterpret_cast<uintptr_t>(scales + 64 * (wave + 4 * r))),
+                                     4, 0, 0);
+  }
   if constexpr (QV_DMA) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
@@ -280,29 +311,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
   constexpr int kOutRowBytes = WN * (int)sizeof(OutT) + (kBF16Out ? 8 : 16);
   __syncthreads();  // every wave is done with the stage buffers
   uint8_t* stage_out = lds + wave * (WM * kOutRowBytes);
+  // Row scales carry the 2^-8 of the accumulator (256 acc converts to fp32 exactly, |256 acc| <
+  // 2^26 with its low 8 bits zero); a row scale below 2^-118 becomes subnormal and keeps at least
+  // 16 significant bits.
   float sa[FM];
 #pragma unroll
-  for (int c = 0; c < FM; ++c) {
-    const int64_t m = m0 + wm * WM + 32 * c + r32;
-    sa[c] = x_scale[m < M ? m : M - 1];
-  }
+  for (int c = 0; c < FM; ++c) sa[c] = scales[BN + wm * WM + 32 * c + r32] * 0.00390625f;
 #pragma unroll
   for (int a = 0; a < FN; ++a) {
 #pragma unroll
     for (int vg = 0; vg < 4; ++vg) {
       const int nl = 32 * a + 8 * vg + 4 * h;  // column inside the wave block
-      const int64_t n = n0 + wn * WN + nl;
-      const float4 sw4 = *reinterpret_cast<const float4*>(w_scale + n);
-      const float4 b4 = bias ? *reinterpret_cast<const float4*>(bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 sw4 = *reinterpret_cast<const float4*>(scales + wn * WN + nl);
       const float sw[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
-      const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+      float bb[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kBias) {
+        const float4 b4 = *reinterpret_cast<const float4*>(bias + n0 + wn * WN + nl);
+        bb[0] = b4.x; bb[1] = b4.y; bb[2] = b4.z; bb[3] = b4.w;
+      }
 #pragma unroll
       for (int c = 0; c < FM; ++c) {
         const int ml = 32 * c + r32;  // row inside the wave block
         float y[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          y[v] = (float)(acc[a][c][4 * vg + v] >> 8) * sa[c] * sw[v] + bb[v];
+          y[v] = (float)acc[a][c][4 * vg + v] * sa[c] * sw[v];
+          if constexpr (kBias) y[v] += bb[v];
           if constexpr (kGelu) y[v] = gelu(y[v]);
         }
         uint8_t* dst = stage_out + ml * kOutRowBytes + nl * (int)sizeof(OutT);
@@ -335,24 +369,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
   }
 }
 
-template <int BN, int BM, int RB, int STAGES, bool kBF16Out, bool kGelu>
+template <int BN, int BM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias>
 hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
                     int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
-  constexpr size_t kStageLds = (size_t)STAGES * (BN + BM) * RB;
-  constexpr size_t kOutLds = 4 * (size_t)(BM / 2) * ((BN / 2) * (kBF16Out ? 2 : 4) + (kBF16Out ? 8 : 16));
-  constexpr size_t kLds = kStageLds > kOutLds ? kStageLds : kOutLds;
+  constexpr size_t kLds = GemmLds<BN, BM, RB, STAGES, kBF16Out>::kTotal;
   static int attr_set[16] = {0};  // per device: allow more than 64 KB of dynamic LDS once
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
   if (!attr_set[dev]) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a4_gemm_kernel<BN, BM, RB, STAGES, kBF16Out, kGelu>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&w4a4_gemm_kernel<BN, BM, RB, STAGES, kBF16Out, kGelu, kBias>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
     if (e != hipSuccess) return e;
     attr_set[dev] = 1;
   }
   const int64_t blocks = (N / BN) * ((M + BM - 1) / BM);
-  hipLaunchKernelGGL((w4a4_gemm_kernel<BN, BM, RB, STAGES, kBF16Out, kGelu>), dim3((unsigned)blocks), dim3(kThreads), kLds,
-                     st, Xq, xs, Wq, ws, bias, M, N, K, Y, ldy);
+  hipLaunchKernelGGL((w4a4_gemm_kernel<BN, BM, RB, STAGES, kBF16Out, kGelu, kBias>), dim3((unsigned)blocks),
+                     dim3(kThreads), kLds, st, Xq, xs, Wq, ws, bias, M, N, K, Y, ldy);
   return hipGetLastError();
 }
 
@@ -365,16 +398,16 @@ hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const
 constexpr int kTileN = QV_TILE_N, kTileM = QV_TILE_M;
 
 
-template <bool kBF16Out, bool kGelu>
+template <bool kBF16Out, bool kGelu, bool kBias>
 hipError_t launch_k(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
                     int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
   // 128 codes (64 bytes of every row) per stage; a 256-code stage variant is kept selectable for
   // measurements (it halves the barriers but its 64 KB ring leaves two blocks per CU).
   if constexpr (QV_RB128) {
     if ((K % 256) == 0)
-      return launch_t<kTileN, kTileM, 128, QV_STAGES_128, kBF16Out, kGelu>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+      return launch_t<kTileN, kTileM, 128, QV_STAGES_128, kBF16Out, kGelu, kBias>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
   }
-  return launch_t<kTileN, kTileM, 64, QV_STAGES, kBF16Out, kGelu>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+  return launch_t<kTileN, kTileM, 64, QV_STAGES, kBF16Out, kGelu, kBias>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
 }
 
 }  // namespace
@@ -382,12 +415,20 @@ hipError_t launch_k(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const
 hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws,
                             const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out,
                             int64_t ldy, hipStream_t st) {
-  if (bf16_out) {
-    return gelu ? launch_k<true, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
-                : launch_k<true, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+  if (bias) {
+    if (bf16_out) {
+      return gelu ? launch_k<true, true, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
+                  : launch_k<true, false, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+    }
+    return gelu ? launch_k<false, true, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
+                : launch_k<false, false, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
   }
-  return gelu ? launch_k<false, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
-              : launch_k<false, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+  if (bf16_out) {
+    return gelu ? launch_k<true, true, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
+                : launch_k<true, false, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+  }
+  return gelu ? launch_k<false, true, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
+              : launch_k<false, false, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
 }
 
 }  // namespace qv

@@ -182,6 +182,21 @@ def test_gemm_extreme_codes(qv, dev, fa, fw):
     assert np.all(Y == fa * fw * K)
 
 
+def test_gemm_tiny_row_scales(qv, dev):
+    """Row scales just above the fp32 normal minimum (the epilogue folds 2^-8 into them, which makes
+    them subnormal there) still give outputs within the relative bound."""
+    M, N, K = 130, 256, 1024
+    rng = np.random.default_rng(11)
+    Xq, Wq = random_packed(M, K, rng), random_packed(N, K, rng)
+    xs = (rng.uniform(1.0, 2.0, M) * 2.0 ** rng.integers(-126, -116, M)).astype(np.float32)
+    xs[:4] = [2.0 ** -126, 1.2345 * 2.0 ** -124, 1.999 * 2.0 ** -119, 3.0]
+    ws = rng.uniform(0.001, 0.02, N).astype(np.float32)
+    for epi in (0, 1):
+        Y = run_gemm(qv, dev, Xq, xs, Wq, ws, None, epi, "fp32")
+        Y_ref = oracle.w4a4_gemm(Xq, xs, Wq, ws, None, epi)
+        acc.check_outputs(Y, Y_ref, False, f"tiny row scales epi={epi}")
+
+
 @pytest.mark.parametrize("epi,out,bias,pad", [(0, "fp32", False, 0), (1, "fp32", False, 0), (0, "bf16", False, 0),
                                               (1, "bf16", True, 64), (0, "fp32", True, 32)])
 def test_gemm_epilogue_parity(qv, dev, epi, out, bias, pad):
