@@ -35,6 +35,8 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=50,
                    help="untimed steps first: the GPU clock needs tens of milliseconds of load to ramp up from idle")
     p.add_argument("--workload", default="block_32frames")
+    p.add_argument("--secondary", default="qkv_8frames",
+                   help="a second workload timed the same way after the main one ('' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
     p.add_argument("--no-bf16-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=256, help="rows per linear in the oracle sample")
@@ -263,6 +265,30 @@ def main():
                       f"explicit-matrix fp64 rotation, fp32 quantization, int64 triple-loop GEMM, fp64 "
                       f"dequant/GELU), single thread, {t_cpu:.1f} s",
             "host_cpus": os.cpu_count()}
+
+    # ---------------------------------------------------------------- secondary workload
+    if args.secondary and args.secondary != wl.name:
+        del layers
+        torch.cuda.empty_cache()
+        wl2 = WORKLOADS[args.secondary]
+        layers2 = workload.build(qv, wl2, dev, share_outputs=wl2.blocks > 1)
+
+        def step2():
+            for L in layers2:
+                workload.run_linear(qv, L, stream)
+
+        for _ in range(args.warmup):
+            step2()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step2()
+        torch.cuda.synchronize()
+        w2 = (time.perf_counter() - t0) / args.steps
+        ops2 = sum(2.0 * wl2.M * L.lin.N * L.lin.K for L in layers2)
+        result["secondary"] = {"workload": wl2.name, "description": wl2.description,
+                               "value": round(ops2 / w2 / 1e12, 2), "unit": "TOPS", "ms_per_step": round(1e3 * w2, 4)}
+        del layers2
 
     print(json.dumps(result))
 
