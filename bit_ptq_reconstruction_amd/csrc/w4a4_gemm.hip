@@ -56,7 +56,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #define QV_STAGES_128 2  // ring depth with 256 codes per stage
 #endif
 
-constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 
 // XOR swizzle of the 16-byte units of a tile row (U units per row): conflict-free fragment reads
@@ -106,32 +105,42 @@ __device__ __forceinline__ float gelu(float y) {
 
 // LDS of a block: the stage ring (reused for output staging in the epilogue), then the tile's
 // BN weight scales and BM activation scales, fetched by LDS-DMA when the tile starts.
-template <int BN, int BM, int RB, int STAGES, bool kBF16Out>
+template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out>
 struct GemmLds {
   static constexpr size_t kStage = (size_t)STAGES * (BN + BM) * RB;
-  static constexpr size_t kOut = 4 * (size_t)(BM / 2) * ((BN / 2) * (kBF16Out ? 2 : 4) + (kBF16Out ? 8 : 16));
+  static constexpr size_t kOut =
+      (size_t)WGN * WGM * (BM / WGM) * ((BN / WGN) * (kBF16Out ? 2 : 4) + (kBF16Out ? 8 : 16));
   static constexpr size_t kScaleOffset = kStage > kOut ? kStage : kOut;
   static constexpr size_t kTotal = kScaleOffset + 4 * (size_t)(BN + BM);
 };
 
-template <int BN, int BM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 128 ? 2 : 3))) void w4a4_gemm_kernel(const uint8_t* __restrict__ Xq,
+// Waves per SIMD the register allocation must allow: three 4-wave blocks of 64 x 64 wave tiles per
+// CU; two waves per SIMD for the larger wave tiles (128 accumulator registers each).
+template <int BN, int BM, int WGN, int WGM, int RB>
+constexpr int waves_per_eu() {
+  return (RB == 128 || (BN / WGN) * (BM / WGM) > 4096) ? 2 : (WGN * WGM == 8 ? 4 : 3);
+}
+
+template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias>
+__global__ __launch_bounds__(64 * WGN * WGM)
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB>()))) void w4a4_gemm_kernel(const uint8_t* __restrict__ Xq,
                                                             const float* __restrict__ x_scale,
                                                             const uint8_t* __restrict__ Wq,
                                                             const float* __restrict__ w_scale,
                                                             const float* __restrict__ bias, int64_t M,
                                                             int64_t N, int64_t K, void* __restrict__ Y,
                                                             int64_t ldy) {
-  constexpr int WN = BN / 2, WM = BM / 2;  // wave sub-tile
+  constexpr int kWaves = WGN * WGM, kThr = 64 * kWaves;
+  constexpr int WN = BN / WGN, WM = BM / WGM;  // wave sub-tile
   constexpr int FN = WN / 32, FM = WM / 32;
   constexpr int kRowBytes = RB;   // packed bytes of one tile row per stage (2 RB codes)
   constexpr int U = RB / 16;      // 16-byte units per tile row and stage
   constexpr int kSub = RB / 16;   // K32 MFMA sub-steps per stage
   constexpr int kReads = RB / 32; // ds_read_b128 per fragment per stage
   constexpr int kUnits = (BN + BM) * U;  // 16-byte units per stage
-  constexpr int kLoads = kUnits / kThreads;              // LDS-direct loads per lane per stage
+  constexpr int kLoads = kUnits / kThr;                  // LDS-direct loads per lane per stage
   constexpr int kStageBytes = (BN + BM) * kRowBytes;
-  static_assert(kUnits % kThreads == 0, "tile must split evenly over the waves");
+  static_assert(kUnits % kThr == 0, "tile must split evenly over the waves");
   static_assert(STAGES >= 2 && (STAGES - 2) * kLoads < 64, "pipeline depth");
   static_assert((BN + BM) % 64 == 0, "whole waves of scale loads");
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % WGN, wm = wave / WGN;
 
   // XCD-major tile order.
   const int64_t tiles_n = N / BN;
@@ -154,11 +163,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
   const int64_t m0 = tile_m * BM;
   const int64_t row_bytes = K / 2;
 
-  // Source of each of this lane's loads; LDS unit P = 64 * (4 i + wave) + lane of the stage buffer.
+  // Source of each of this lane's loads; LDS unit P = 64 * (kWaves i + wave) + lane of the stage
+  // buffer.
   const uint8_t* src[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
-    const int P = 64 * (4 * i + wave) + lane;
+    const int P = 64 * (kWaves * i + wave) + lane;
     const int r = P / U;  // row inside the combined A|B tile
     if (r < BN) {
       src[i] = Wq + (n0 + r) * row_bytes + 16 * ((P % U) ^ swz<U>(r));
@@ -170,7 +180,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
     }
   }
   // Stage loads.  With LDS-DMA (global_load_lds_dwordx4) the 16 bytes of lane l land at unit
-  // 64 * (4 i + wave) + l of the stage buffer directly; otherwise they are fetched into registers
+  // 64 * (kWaves i + wave) + l of the stage buffer directly; otherwise they are fetched into registers
   // (fetch_stage) and written to the same units with ds_write_b128 (store_stage).
   u32x4 staged[kLoads];
   auto fetch_stage = [&](int64_t kb) {
@@ -180,12 +190,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
   auto store_stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
-      *reinterpret_cast<u32x4*>(lds + buf * kStageBytes + 1024 * (4 * i + wave) + 16 * lane) = staged[i];
+      *reinterpret_cast<u32x4*>(lds + buf * kStageBytes + 1024 * (kWaves * i + wave) + 16 * lane) = staged[i];
   };
   auto issue_stage = [&](int buf, int64_t kb) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      uint8_t* dst = lds + buf * kStageBytes + 1024 * (4 * i + wave);
+      uint8_t* dst = lds + buf * kStageBytes + 1024 * (kWaves * i + wave);
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[i] + kb),
                                        reinterpret_cast<__attribute__((address_space(3))) void*>(
                                            reinterpret_cast<uintptr_t>(dst)),
@@ -205,13 +215,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
   const int nk = (int)(K / (2 * kRowBytes));
 
   // The tile's scales: scale slot i holds w_scale[n0 + i] (i < BN) or x_scale[m0 + i - BN] (rows
-  // past M repeat the last row); thread t fetches slots t, t + 256, ...  Issued before the stage
+  // past M repeat the last row); thread t fetches slots t, t + kThr, ...  Issued before the stage
   // loads, so the first iteration's vmcnt wait covers them.
-  float* const scales = reinterpret_cast<float*>(lds + GemmLds<BN, BM, RB, STAGES, kBF16Out>::kScaleOffset);
+  float* const scales = reinterpret_cast<float*>(lds + GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out>::kScaleOffset);
 #pragma unroll
-  for (int r = 0; r < (BN + BM + kThreads - 1) / kThreads; ++r) {
-    const int i = tid + kThreads * r;
-    if (kThreads * r + 64 * wave >= BN + BM) break;  // wave-uniform
+  for (int r = 0; r < (BN + BM + kThr - 1) / kThr; ++r) {
+    const int i = tid + kThr * r;
+    if (kThr * r + 64 * wave >= BN + BM) break;  // wave-uniform
     const float* sp;
     if (i < BN) {
       sp = w_scale + n0 + i;
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
     }
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(sp),
                                      reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                         reinterpret_cast<uintptr_t>(scales + 64 * (wave + 4 * r))),
+                                         reinterpret_cast<uintptr_t>(scales + 64 * (wave + kWaves * r))),
                                      4, 0, 0);
   }
   if constexpr (QV_DMA) {
@@ -308,9 +318,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
   // by 8 or 16 bytes so the staging writes spread over the banks); the block is then written with
   // 16-byte non-temporal stores, each group of lanes covering whole contiguous row segments.
   using OutT = typename std::conditional<kBF16Out, uint16_t, float>::type;
-  constexpr int kOutRowBytes = WN * (int)sizeof(OutT) + (kBF16Out ? 8 : 16);
-  __syncthreads();  // every wave is done with the stage buffers
-  uint8_t* stage_out = lds + wave * (WM * kOutRowBytes);
+  // Staging without a block barrier: after the last stage's barrier no wave reads any ring buffer
+  // but the last stage's, and every LDS-DMA has landed, so the other STAGES - 1 buffers are free.
+  // When the wave blocks fit there (two waves per 16 KB buffer for 128 x 128 bf16 tiles), each wave
+  // stages at once, in rows of exactly WN outputs whose 16-byte chunks are XOR-swizzled by the row;
+  // otherwise the block synchronizes and stages over the whole ring with padded rows.
+  constexpr int kWaveOutBytes = WM * WN * (int)sizeof(OutT);
+  constexpr bool kFreeStaging = STAGES >= 3 && kStageBytes % kWaveOutBytes == 0 &&
+                                kWaves <= (STAGES - 1) * (kStageBytes / kWaveOutBytes) && WN * (int)sizeof(OutT) == 128;
+  constexpr int kOutRowBytes = WN * (int)sizeof(OutT) + (kFreeStaging ? 0 : (kBF16Out ? 8 : 16));
+  uint8_t* stage_out;
+  if constexpr (kFreeStaging) {
+    constexpr int kPerBuf = kStageBytes / kWaveOutBytes;  // wave blocks per free buffer
+    const int slot = wave / kPerBuf;                      // index among the free buffers
+    const int buf = (nk + slot) % STAGES;                 // skips (nk - 1) % STAGES, the last stage
+    stage_out = lds + buf * kStageBytes + (wave % kPerBuf) * kWaveOutBytes;
+  } else {
+    __syncthreads();  // every wave is done with the stage buffers
+    stage_out = lds + wave * (WM * kOutRowBytes);
+  }
+  // Byte offset of the 16-byte chunk ch of row ml in the staging block.
+  auto chunk_at = [&](int ml, int ch) {
+    if constexpr (kFreeStaging) return ml * kOutRowBytes + 16 * (ch ^ (ml & 7));
+    else return ml * kOutRowBytes + 16 * ch;
+  };
   // Row scales carry the 2^-8 of the accumulator (256 acc converts to fp32 exactly, |256 acc| <
   // 2^26 with its low 8 bits zero); a row scale below 2^-118 becomes subnormal and keeps at least
   // 16 significant bits.
@@ -339,7 +370,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
           if constexpr (kBias) y[v] += bb[v];
           if constexpr (kGelu) y[v] = gelu(y[v]);
         }
-        uint8_t* dst = stage_out + ml * kOutRowBytes + nl * (int)sizeof(OutT);
+        uint8_t* dst = stage_out + chunk_at(ml, nl * (int)sizeof(OutT) / 16) + (nl * (int)sizeof(OutT)) % 16;
         if constexpr (kBF16Out) {
           const bf16x2 lo = __builtin_convertvector((f32x2{y[0], y[1]}), bf16x2);
           const bf16x2 hi = __builtin_convertvector((f32x2{y[2], y[3]}), bf16x2);
@@ -361,7 +392,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
     const int ml = pass * kRowsPerPass + lane / kChunksPerRow;
     const int ch = lane % kChunksPerRow;
     const int64_t m = m0 + wm * WM + ml;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(stage_out + ml * kOutRowBytes + 16 * ch);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage_out + chunk_at(ml, ch));
     if (m < M) {
       uint8_t* out = reinterpret_cast<uint8_t*>(static_cast<OutT*>(Y) + m * ldy + n0 + wn * WN) + 16 * ch;
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out));
@@ -369,45 +400,69 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
   }
 }
 
-template <int BN, int BM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias>
+template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias>
 hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
                     int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
-  constexpr size_t kLds = GemmLds<BN, BM, RB, STAGES, kBF16Out>::kTotal;
+  constexpr size_t kLds = GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out>::kTotal;
   static int attr_set[16] = {0};  // per device: allow more than 64 KB of dynamic LDS once
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
   if (!attr_set[dev]) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&w4a4_gemm_kernel<BN, BM, RB, STAGES, kBF16Out, kGelu, kBias>),
+        reinterpret_cast<const void*>(&w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
     if (e != hipSuccess) return e;
     attr_set[dev] = 1;
   }
   const int64_t blocks = (N / BN) * ((M + BM - 1) / BM);
-  hipLaunchKernelGGL((w4a4_gemm_kernel<BN, BM, RB, STAGES, kBF16Out, kGelu, kBias>), dim3((unsigned)blocks),
-                     dim3(kThreads), kLds, st, Xq, xs, Wq, ws, bias, M, N, K, Y, ldy);
+  hipLaunchKernelGGL((w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias>), dim3((unsigned)blocks),
+                     dim3(64 * WGN * WGM), kLds, st, Xq, xs, Wq, ws, bias, M, N, K, Y, ldy);
   return hipGetLastError();
 }
 
-// 128 x 128 tiles (64 x 64 per wave): about 160 registers per lane and 48 KB of LDS, so three
-// blocks share a CU and one block's barrier, prologue and epilogue overlap another's MFMAs.
-#ifndef QV_TILE_N
-#define QV_TILE_N 128
-#define QV_TILE_M 128
+// Tile configurations (block tile BN x BM, wave grid WGN x WGM):
+//   0: 128 x 128, 2 x 2 waves of 64 x 64: 134 registers and 49 KB of LDS, three blocks per CU, so
+//      one block's barrier, prologue and epilogue overlap the others' MFMAs;
+//   1: 256 x 256, 2 x 4 waves of 128 x 64; 2: 256 x 256, 4 x 2 waves of 64 x 128 (one block per
+//      CU, half the LDS-DMA bytes per MFMA);
+//   3: 256 x 128, 4 x 2 waves of 64 x 64; 4: 128 x 256, 2 x 4 waves of 64 x 64.
+// A configuration whose BN does not divide N, and every fp32-output launch, uses configuration 0.
+#ifndef QV_TILE_CFG
+#define QV_TILE_CFG 0
 #endif
-constexpr int kTileN = QV_TILE_N, kTileM = QV_TILE_M;
 
-
-template <bool kBF16Out, bool kGelu, bool kBias>
-hipError_t launch_k(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
-                    int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
+template <int BN, int BM, int WGN, int WGM, bool kBF16Out, bool kGelu, bool kBias>
+hipError_t launch_cfg(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
+                      int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
   // 128 codes (64 bytes of every row) per stage; a 256-code stage variant is kept selectable for
   // measurements (it halves the barriers but its 64 KB ring leaves two blocks per CU).
   if constexpr (QV_RB128) {
     if ((K % 256) == 0)
-      return launch_t<kTileN, kTileM, 128, QV_STAGES_128, kBF16Out, kGelu, kBias>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+      return launch_t<BN, BM, WGN, WGM, 128, QV_STAGES_128, kBF16Out, kGelu, kBias>(Xq, xs, Wq, ws, bias, M, N, K, Y,
+                                                                                 ldy, st);
   }
-  return launch_t<kTileN, kTileM, 64, QV_STAGES, kBF16Out, kGelu, kBias>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+  return launch_t<BN, BM, WGN, WGM, 64, QV_STAGES, kBF16Out, kGelu, kBias>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+}
+
+template <bool kBF16Out, bool kGelu, bool kBias>
+hipError_t launch_k(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
+                    int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
+#define QV_LAUNCH(BN, BM, WGN, WGM) \
+  launch_cfg<BN, BM, WGN, WGM, kBF16Out, kGelu, kBias>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
+  if constexpr (!kBF16Out) {
+    // fp32 outputs: the 256-wide tiles' output staging would not fit in LDS
+    return QV_LAUNCH(128, 128, 2, 2);
+  } else if constexpr (QV_TILE_CFG == 1) {
+    if (N % 256 == 0) return QV_LAUNCH(256, 256, 2, 4);
+  } else if constexpr (QV_TILE_CFG == 2) {
+    if (N % 256 == 0) return QV_LAUNCH(256, 256, 4, 2);
+  } else if constexpr (QV_TILE_CFG == 3) {
+    if (N % 256 == 0) return QV_LAUNCH(256, 128, 4, 2);
+  } else if constexpr (QV_TILE_CFG == 4) {
+    return QV_LAUNCH(128, 256, 2, 4);
+  }
+  return QV_LAUNCH(128, 128, 2, 2);
+#undef QV_LAUNCH
 }
 
 }  // namespace
