@@ -197,6 +197,28 @@ def test_gemm_tiny_row_scales(qv, dev):
         acc.check_outputs(Y, Y_ref, False, f"tiny row scales epi={epi}")
 
 
+@pytest.mark.parametrize("K,epi,bias", [(256, 0, False), (256, 1, True), (1024, 0, False)])
+def test_gemm_many_tiles_per_block(qv, dev, K, epi, bias):
+    """bf16 outputs over more tiles than resident blocks (each block walks several tiles, its LDS ring
+    streaming across tile boundaries), down to two stages per tile, with a ragged last row tile;
+    every output of a sample of rows is checked."""
+    M, N = 128 * 1700 + 77, 256
+    rng = np.random.default_rng(K + epi)
+    Xq, Wq = random_packed(M, K, rng), random_packed(N, K, rng)
+    xs = rng.uniform(0.01, 0.1, M).astype(np.float32)
+    ws = rng.uniform(0.01, 0.1, N).astype(np.float32)
+    b = rng.standard_normal(N).astype(np.float32) if bias else None
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    qv.qv_w4a4_gemm(t(Xq), t(xs), t(Wq), t(ws), None if b is None else t(b), Y, epi)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 200, M), rng.choice(M, 300, replace=False)]))
+    Yr = Y[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+    Y_ref = oracle.w4a4_gemm(Xq[rows], xs[rows], Wq, ws, b, epi)
+    acc.check_outputs(Yr, Y_ref, True, f"many tiles K={K} epi={epi} bias={bias}")
+    assert not torch.isnan(Y.float()).any(), "an output element was not written"
+
+
 @pytest.mark.parametrize("epi,out,bias,pad", [(0, "fp32", False, 0), (1, "fp32", False, 0), (0, "bf16", False, 0),
                                               (1, "bf16", True, 64), (0, "fp32", True, 32)])
 def test_gemm_epilogue_parity(qv, dev, epi, out, bias, pad):
