@@ -35,6 +35,7 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=50,
                    help="untimed steps first: the GPU clock needs tens of milliseconds of load to ramp up from idle")
     p.add_argument("--workload", default="block_32frames")
+    p.add_argument("--no-w8a8", dest="w8a8", action="store_false", help="skip the W8A8 line")
     p.add_argument("--secondary", default="qkv_8frames",
                    help="a second workload timed the same way after the main one ('' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
@@ -289,6 +290,34 @@ def main():
         result["secondary"] = {"workload": wl2.name, "description": wl2.description,
                                "value": round(ops2 / w2 / 1e12, 2), "unit": "TOPS", "ms_per_step": round(1e3 * w2, 4)}
         del layers2
+
+    # ---------------------------------------------------------------- W8A8 on the same workload
+    if args.w8a8:
+        torch.cuda.empty_cache()
+        layers8 = workload.build(qv, wl, dev, share_outputs=wl.blocks > 1, bits=8)
+
+        def step8():
+            for L in layers8:
+                workload.run_linear(qv, L, stream)
+
+        for _ in range(args.warmup):
+            step8()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step8()
+        torch.cuda.synchronize()
+        w8 = (time.perf_counter() - t0) / args.steps
+        g8 = timed(lambda: [qv.qv_w8a8_gemm(L.Xq, L.xs, L.Wq, L.ws, None, L.Y, L.lin.epi, stream)
+                            for _ in range(reps) for L in layers8]) / (reps * len(layers8))
+        q8 = timed(lambda: [qv.qv_hadamard_smooth_quant8(L.X, L.inv, L.Xq, L.xs, stream)
+                            for _ in range(reps) for L in layers8]) / (reps * len(layers8))
+        b8 = sum(M * L.lin.K * L.X.element_size() + M * L.lin.K + 4 * M for L in layers8) / len(layers8)
+        result["w8a8"] = {"what": "the same workload with 8-bit codes (scale absmax/127, int8 MFMA without unpacking)",
+                          "value": round(ops_per_step / w8 / 1e12, 2), "unit": "TOPS", "ms_per_step": round(1e3 * w8, 4),
+                          "gemm_TOPS": round(k2_ops / g8 / 1e12, 2), "gemm_frac": round(k2_ops / g8 / 1e12 / PEAK_INT8_TOPS, 4),
+                          "rotate_quant_GBps": round(b8 / q8 / 1e9, 1)}
+        del layers8
 
     print(json.dumps(result))
 

@@ -57,8 +57,15 @@ def lib():
         L.qv_w4a4_linear_workspace_size.restype = sz
         L.qv_w4a4_linear.argtypes = [P, i32, i64, i64, i64, P, P, P, P, i64, i32, P, i32, i64, P, sz, P]
         L.qv_smooth_calibrate.argtypes = [P, i32, i64, i64, P, i32, i64, i64, i64, f32, P, P, P]
+        L.qv_hadamard_smooth_quant8.argtypes = [P, i32, i64, i64, i64, P, P, P, P]
+        L.qv_pack_weights8.argtypes = [P, i32, i64, i64, i64, P, P, P, P]
+        L.qv_w8a8_gemm.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P, i32, i64, P]
+        L.qv_w8a8_linear_workspace_size.argtypes = [i64, i64]
+        L.qv_w8a8_linear_workspace_size.restype = sz
+        L.qv_w8a8_linear.argtypes = [P, i32, i64, i64, i64, P, P, P, P, i64, i32, P, i32, i64, P, sz, P]
         for name in ("qv_hadamard_smooth_quant", "qv_pack_weights", "qv_w4a4_gemm", "qv_w4a4_linear",
-                     "qv_smooth_calibrate"):
+                     "qv_smooth_calibrate", "qv_hadamard_smooth_quant8", "qv_pack_weights8", "qv_w8a8_gemm",
+                     "qv_w8a8_linear"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -144,3 +151,41 @@ def qv_smooth_calibrate(Xc, W, smooth, inv_smooth, alpha: float = 0.5, stream=No
     _check(lib().qv_smooth_calibrate(_ptr(Xc), _dtype(Xc), Mc, _ld(Xc), _ptr(W), _dtype(W), N, _ld(W), K,
                                      float(alpha), _ptr(smooth), _ptr(inv_smooth), _stream(stream)),
            "qv_smooth_calibrate")
+
+
+# ------------------------------------------------------------------------------------------- W8A8
+
+def qv_hadamard_smooth_quant8(X, inv_smooth, Xq8, x_scale, stream=None) -> None:
+    """X [M, K] fp32/bf16 -> Xq8 [M, K] int8 codes, x_scale [M] fp32 (scale absmax / 127)."""
+    M, K = X.shape
+    _check(lib().qv_hadamard_smooth_quant8(_ptr(X), _dtype(X), M, K, _ld(X), _ptr(inv_smooth), _ptr(Xq8),
+                                           _ptr(x_scale), _stream(stream)), "qv_hadamard_smooth_quant8")
+
+
+def qv_pack_weights8(W, smooth, Wq8, w_scale, stream=None) -> None:
+    """W [N, K] fp32/bf16 -> Wq8 [N, K] int8 codes, w_scale [N] fp32."""
+    N, K = W.shape
+    _check(lib().qv_pack_weights8(_ptr(W), _dtype(W), N, K, _ld(W), _ptr(smooth), _ptr(Wq8), _ptr(w_scale),
+                                  _stream(stream)), "qv_pack_weights8")
+
+
+def qv_w8a8_gemm(Xq8, x_scale, Wq8, w_scale, bias, Y, epi: int = QV_EPI_NONE, stream=None) -> None:
+    """Y [M, N] (fp32/bf16) = dequant(Xq8 . Wq8^T) (+ bias) (+ GELU)."""
+    M, K = Xq8.shape
+    N = Wq8.shape[0]
+    _check(lib().qv_w8a8_gemm(_ptr(Xq8), _ptr(x_scale), _ptr(Wq8), _ptr(w_scale), _ptr(bias), M, N, K, int(epi),
+                              _ptr(Y), _dtype(Y), _ld(Y), _stream(stream)), "qv_w8a8_gemm")
+
+
+def qv_w8a8_linear_workspace_size(M: int, K: int) -> int:
+    return int(lib().qv_w8a8_linear_workspace_size(int(M), int(K)))
+
+
+def qv_w8a8_linear(X, inv_smooth, Wq8, w_scale, bias, Y, workspace, epi: int = QV_EPI_NONE, stream=None) -> None:
+    """The whole online W8A8 layer; ``workspace`` holds at least ``qv_w8a8_linear_workspace_size(M, K)`` bytes."""
+    M, K = X.shape
+    N = Wq8.shape[0]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().qv_w8a8_linear(_ptr(X), _dtype(X), M, K, _ld(X), _ptr(inv_smooth), _ptr(Wq8), _ptr(w_scale),
+                                _ptr(bias), N, int(epi), _ptr(Y), _dtype(Y), _ld(Y), _ptr(workspace), nbytes,
+                                _stream(stream)), "qv_w8a8_linear")

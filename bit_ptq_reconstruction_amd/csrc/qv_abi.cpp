@@ -21,7 +21,7 @@ bool valid_dtype(qv_dtype t) { return t == QV_F32 || t == QV_BF16; }
 
 // Shared checks of the rotate-quantize step (activation or weight side).
 qv_status check_rotate_quant(const void* X, qv_dtype dt, int64_t rows, int64_t K, int64_t ld, const float* mult,
-                             const uint8_t* q, const float* scale) {
+                             const void* q, const float* scale) {
   if (!valid_dtype(dt)) return QV_ERR_DTYPE;
   if (rows < 0 || K <= 0) return QV_ERR_SHAPE;
   if (K != 1024 && K != 4096) return QV_ERR_UNSUPPORTED;
@@ -32,11 +32,13 @@ qv_status check_rotate_quant(const void* X, qv_dtype dt, int64_t rows, int64_t K
   return QV_OK;
 }
 
-qv_status check_gemm(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
-                     int64_t M, int64_t N, int64_t K, qv_epilogue epi, const void* Y, qv_dtype yt, int64_t ldy) {
+// k_step: 128 for packed int4 operands (one 64-byte stage), 64 for int8 operands.
+qv_status check_gemm(const void* Xq, const float* xs, const void* Wq, const float* ws, const float* bias,
+                     int64_t M, int64_t N, int64_t K, qv_epilogue epi, const void* Y, qv_dtype yt, int64_t ldy,
+                     int64_t k_step = 128) {
   if (!valid_dtype(yt) || (epi != QV_EPI_NONE && epi != QV_EPI_GELU)) return QV_ERR_DTYPE;
   if (M < 0 || N < 0 || K <= 0) return QV_ERR_SHAPE;
-  if ((K % 128) != 0 || K > 65536 || (N % 128) != 0) return QV_ERR_UNSUPPORTED;
+  if ((K % k_step) != 0 || K > 65536 || (N % 128) != 0) return QV_ERR_UNSUPPORTED;
   if (ldy < N) return QV_ERR_SHAPE;
   if (M == 0 || N == 0) return QV_OK;
   if (!Xq || !xs || !Wq || !ws || !Y) return QV_ERR_NULL;
@@ -74,7 +76,7 @@ qv_status qv_hadamard_smooth_quant(const void* X, qv_dtype x_dtype, int64_t M, i
   try {
     qv_status st = check_rotate_quant(X, x_dtype, M, K, ldx, inv_smooth, Xq, x_scale);
     if (st != QV_OK || M == 0) return st;
-    return hip_status(qv::launch_rotate_quant(X, x_dtype == QV_BF16, M, K, ldx, inv_smooth, Xq, x_scale,
+    return hip_status(qv::launch_rotate_quant(X, x_dtype == QV_BF16, M, K, ldx, inv_smooth, Xq, x_scale, 4,
                                               static_cast<hipStream_t>(hip_stream)));
   } catch (...) {
     return QV_ERR_INTERNAL;
@@ -86,7 +88,7 @@ qv_status qv_pack_weights(const void* W, qv_dtype w_dtype, int64_t N, int64_t K,
   try {
     qv_status st = check_rotate_quant(W, w_dtype, N, K, ldw, smooth, Wq, w_scale);
     if (st != QV_OK || N == 0) return st;
-    return hip_status(qv::launch_rotate_quant(W, w_dtype == QV_BF16, N, K, ldw, smooth, Wq, w_scale,
+    return hip_status(qv::launch_rotate_quant(W, w_dtype == QV_BF16, N, K, ldw, smooth, Wq, w_scale, 4,
                                               static_cast<hipStream_t>(hip_stream)));
   } catch (...) {
     return QV_ERR_INTERNAL;
@@ -130,7 +132,7 @@ qv_status qv_w4a4_linear(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, 
     uint8_t* xq = static_cast<uint8_t*>(workspace);
     float* xs = reinterpret_cast<float*>(xq + round256(static_cast<size_t>(M) * static_cast<size_t>(K / 2)));
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    st = hip_status(qv::launch_rotate_quant(X, x_dtype == QV_BF16, M, K, ldx, inv_smooth, xq, xs, s));
+    st = hip_status(qv::launch_rotate_quant(X, x_dtype == QV_BF16, M, K, ldx, inv_smooth, xq, xs, 4, s));
     if (st != QV_OK) return st;
     return hip_status(
         qv::launch_w4a4_gemm(xq, xs, Wq, w_scale, bias, M, N, K, epi == QV_EPI_GELU, Y, y_dtype == QV_BF16, ldy, s));
@@ -155,6 +157,79 @@ qv_status qv_smooth_calibrate(const void* Xc, qv_dtype xc_dtype, int64_t Mc, int
     if (!aligned(smooth) || !aligned(inv_smooth)) return QV_ERR_ALIGN;
     return hip_status(qv::launch_smooth_calibrate(Xc, xc_dtype == QV_BF16, Mc, ldx, W, w_dtype == QV_BF16, N, ldw, K,
                                                   alpha, smooth, inv_smooth, static_cast<hipStream_t>(hip_stream)));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
+qv_status qv_hadamard_smooth_quant8(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                    const float* inv_smooth, int8_t* Xq8, float* x_scale, void* hip_stream) {
+  try {
+    qv_status st = check_rotate_quant(X, x_dtype, M, K, ldx, inv_smooth, Xq8, x_scale);
+    if (st != QV_OK || M == 0) return st;
+    return hip_status(qv::launch_rotate_quant(X, x_dtype == QV_BF16, M, K, ldx, inv_smooth,
+                                              reinterpret_cast<uint8_t*>(Xq8), x_scale, 8,
+                                              static_cast<hipStream_t>(hip_stream)));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
+qv_status qv_pack_weights8(const void* W, qv_dtype w_dtype, int64_t N, int64_t K, int64_t ldw, const float* smooth,
+                           int8_t* Wq8, float* w_scale, void* hip_stream) {
+  try {
+    qv_status st = check_rotate_quant(W, w_dtype, N, K, ldw, smooth, Wq8, w_scale);
+    if (st != QV_OK || N == 0) return st;
+    return hip_status(qv::launch_rotate_quant(W, w_dtype == QV_BF16, N, K, ldw, smooth,
+                                              reinterpret_cast<uint8_t*>(Wq8), w_scale, 8,
+                                              static_cast<hipStream_t>(hip_stream)));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
+qv_status qv_w8a8_gemm(const int8_t* Xq8, const float* x_scale, const int8_t* Wq8, const float* w_scale,
+                       const float* bias, int64_t M, int64_t N, int64_t K, qv_epilogue epi, void* Y,
+                       qv_dtype y_dtype, int64_t ldy, void* hip_stream) {
+  try {
+    qv_status st = check_gemm(Xq8, x_scale, Wq8, w_scale, bias, M, N, K, epi, Y, y_dtype, ldy, 64);
+    if (st != QV_OK || M == 0 || N == 0) return st;
+    return hip_status(qv::launch_w8a8_gemm(Xq8, x_scale, Wq8, w_scale, bias, M, N, K, epi == QV_EPI_GELU, Y,
+                                           y_dtype == QV_BF16, ldy, static_cast<hipStream_t>(hip_stream)));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
+size_t qv_w8a8_linear_workspace_size(int64_t M, int64_t K) {
+  if (M < 0 || K <= 0) return 0;
+  return round256(static_cast<size_t>(M) * static_cast<size_t>(K)) + round256(static_cast<size_t>(M) * 4);
+}
+
+qv_status qv_w8a8_linear(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, int64_t ldx,
+                         const float* inv_smooth, const int8_t* Wq8, const float* w_scale, const float* bias,
+                         int64_t N, qv_epilogue epi, void* Y, qv_dtype y_dtype, int64_t ldy, void* workspace,
+                         size_t workspace_bytes, void* hip_stream) {
+  try {
+    qv_status st = check_rotate_quant(X, x_dtype, M, K, ldx, inv_smooth, reinterpret_cast<uint8_t*>(16),
+                                      reinterpret_cast<float*>(16));
+    if (st != QV_OK) return st;
+    st = check_gemm(reinterpret_cast<int8_t*>(16), reinterpret_cast<float*>(16), Wq8, w_scale, bias, M, N, K, epi, Y,
+                    y_dtype, ldy, 64);
+    if (st != QV_OK) return st;
+    if (M == 0 || N == 0) return QV_OK;
+    const size_t need = qv_w8a8_linear_workspace_size(M, K);
+    if (!workspace || workspace_bytes < need) return QV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) % 256) != 0) return QV_ERR_ALIGN;
+    int8_t* xq = static_cast<int8_t*>(workspace);
+    float* xs = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) +
+                                         round256(static_cast<size_t>(M) * static_cast<size_t>(K)));
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    st = hip_status(qv::launch_rotate_quant(X, x_dtype == QV_BF16, M, K, ldx, inv_smooth,
+                                            reinterpret_cast<uint8_t*>(xq), xs, 8, s));
+    if (st != QV_OK) return st;
+    return hip_status(
+        qv::launch_w8a8_gemm(xq, xs, Wq8, w_scale, bias, M, N, K, epi == QV_EPI_GELU, Y, y_dtype == QV_BF16, ldy, s));
   } catch (...) {
     return QV_ERR_INTERNAL;
   }

@@ -7,13 +7,19 @@
 namespace qv {
 
 // Rotate (Hadamard width K in {1024, 4096}), multiply by mult[k] (NULL = 1), quantize each row to
-// int4 with scale absmax/7 and pack: the activation step and, with the smoothing factors as mult,
-// the weight step.
+// `bits` in {4, 8} with scale absmax / (2^(bits-1) - 1): int4 codes packed two per byte (even k in
+// the low nibble), int8 codes one per byte.  The activation step and, with the smoothing factors as
+// mult, the weight step.
 hipError_t launch_rotate_quant(const void* X, bool bf16, int64_t M, int64_t K, int64_t ld, const float* mult,
-                               uint8_t* q, float* scale, hipStream_t st);
+                               uint8_t* q, float* scale, int bits, hipStream_t st);
 
 // Int4 x int4 GEMM (N % 128 == 0, K % 128 == 0) with dequantization epilogue.
 hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws,
+                            const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out,
+                            int64_t ldy, hipStream_t st);
+
+// Int8 x int8 GEMM (N % 128 == 0, K % 64 == 0) with the same epilogue.
+hipError_t launch_w8a8_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
                             const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out,
                             int64_t ldy, hipStream_t st);
 

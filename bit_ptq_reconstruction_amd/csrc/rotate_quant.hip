@@ -33,7 +33,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #endif
 
 constexpr int kThreads = 256;
-constexpr float kMagic = 12582920.0f;  // 1.5 * 2^23 + 8: its low mantissa byte holds rne(t) + 8
+// 1.5 * 2^23 + 2^(bits-1): fma(x, 1/s, magic) rounds once to nearest-even, and the low mantissa
+// byte of the result is rne(x / s) + 2^(bits-1) (|x / s| <= 2^(bits-1) - 1 keeps it in the byte).
+template <int kBits>
+constexpr float kMagic = 12582912.0f + (float)(1 << (kBits - 1));
 
 // Raw 16-byte chunks of a lane's share of one row: 8 chunks for bf16, 16 for fp32.
 template <typename In>
@@ -91,6 +94,15 @@ __device__ __forceinline__ void load_row(const In* __restrict__ row, int lane, f
 
 // Eight codes (already offset by +8 in the low byte of the magic-rounded floats) -> one dword of
 // two's-complement nibbles, element 2i in the low nibble of byte i.
+// Eight 8-bit codes (low bytes q + 128) -> two dwords of two's-complement bytes, k ascending.
+__device__ __forceinline__ uint2 pack8_int8(const uint32_t (&m)[8]) {
+  const uint32_t a = __builtin_amdgcn_perm(m[1], m[0], 0x0c0c0400u);  // bytes: q0 q1 0 0
+  const uint32_t b = __builtin_amdgcn_perm(m[3], m[2], 0x0c0c0400u);
+  const uint32_t c = __builtin_amdgcn_perm(m[5], m[4], 0x0c0c0400u);
+  const uint32_t d = __builtin_amdgcn_perm(m[7], m[6], 0x0c0c0400u);
+  return make_uint2((a | (b << 16)) ^ 0x80808080u, (c | (d << 16)) ^ 0x80808080u);
+}
+
 __device__ __forceinline__ uint32_t pack8(const uint32_t (&m)[8]) {
   const uint32_t p01 = (m[1] << 4) + m[0];  // low byte: (q1 + 8) << 4 | (q0 + 8)
   const uint32_t p23 = (m[3] << 4) + m[2];
@@ -118,7 +130,7 @@ __device__ __forceinline__ void fill_multiplier_table(const float* __restrict__ 
   }
 }
 
-template <int K, typename In>
+template <int K, typename In, int kBits>
 __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const In* __restrict__ X, int64_t M, int64_t ldx,
                                                                const float* __restrict__ mult,
                                                                uint8_t* __restrict__ Xq,
@@ -174,18 +186,22 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const In* __rest
       }
     }
     amax = row_max<K>(amax);
-    float s = amax / 7.0f;
+    float s = amax / (float)((1 << (kBits - 1)) - 1);
     if (!(s >= 1.17549435e-38f)) s = 0.0f;  // zero or subnormal scale: all-zero row
     const float r = (s > 0.0f) ? 1.0f / s : 0.0f;
 
     if (row < M) {
-      uint32_t* out = reinterpret_cast<uint32_t*>(Xq + row * (K / 2));
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         uint32_t m[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m[e] = __builtin_bit_cast(uint32_t, __builtin_fmaf(v[j][e], r, kMagic));
-        out[dword_index<K>(lane, j)] = pack8(m);
+        for (int e = 0; e < 8; ++e) m[e] = __builtin_bit_cast(uint32_t, __builtin_fmaf(v[j][e], r, kMagic<kBits>));
+        // the lane's eight codes of group j are k = 8 dword_index + 0..7
+        if constexpr (kBits == 4) {
+          reinterpret_cast<uint32_t*>(Xq + row * (K / 2))[dword_index<K>(lane, j)] = pack8(m);
+        } else {
+          reinterpret_cast<uint2*>(Xq + row * K)[dword_index<K>(lane, j)] = pack8_int8(m);
+        }
       }
       if ((lane & (L::kLanesPerRow - 1)) == 0) x_scale[row] = s;
     }
@@ -273,11 +289,11 @@ int grid_for_rows(int64_t M, int rows_per_wave, int resident) {
   return (int)(blocks < resident ? blocks : resident);
 }
 
-template <int K, typename In>
+template <int K, typename In, int kBits>
 hipError_t launch_rq(const void* X, int64_t M, int64_t ld, const float* mult, uint8_t* q, float* scale,
                      hipStream_t st) {
-  const int grid = grid_for_rows(M, RowLayout<K>::kRowsPerWave, resident_grid<rotate_quant_kernel<K, In>>());
-  hipLaunchKernelGGL((rotate_quant_kernel<K, In>), dim3(grid), dim3(kThreads), 0, st,
+  const int grid = grid_for_rows(M, RowLayout<K>::kRowsPerWave, resident_grid<rotate_quant_kernel<K, In, kBits>>());
+  hipLaunchKernelGGL((rotate_quant_kernel<K, In, kBits>), dim3(grid), dim3(kThreads), 0, st,
                      static_cast<const In*>(X), M, ld, mult, q, scale);
   return hipGetLastError();
 }
@@ -293,13 +309,21 @@ hipError_t launch_colmax(const void* X, int64_t M, int64_t ld, unsigned* colmax,
 }  // namespace
 
 hipError_t launch_rotate_quant(const void* X, bool bf16, int64_t M, int64_t K, int64_t ld, const float* mult,
-                               uint8_t* q, float* scale, hipStream_t st) {
-  if (K == 1024) {
-    return bf16 ? launch_rq<1024, uint16_t>(X, M, ld, mult, q, scale, st)
-                : launch_rq<1024, float>(X, M, ld, mult, q, scale, st);
+                               uint8_t* q, float* scale, int bits, hipStream_t st) {
+  if (bits == 8) {
+    if (K == 1024) {
+      return bf16 ? launch_rq<1024, uint16_t, 8>(X, M, ld, mult, q, scale, st)
+                  : launch_rq<1024, float, 8>(X, M, ld, mult, q, scale, st);
+    }
+    return bf16 ? launch_rq<4096, uint16_t, 8>(X, M, ld, mult, q, scale, st)
+                : launch_rq<4096, float, 8>(X, M, ld, mult, q, scale, st);
   }
-  return bf16 ? launch_rq<4096, uint16_t>(X, M, ld, mult, q, scale, st)
-              : launch_rq<4096, float>(X, M, ld, mult, q, scale, st);
+  if (K == 1024) {
+    return bf16 ? launch_rq<1024, uint16_t, 4>(X, M, ld, mult, q, scale, st)
+                : launch_rq<1024, float, 4>(X, M, ld, mult, q, scale, st);
+  }
+  return bf16 ? launch_rq<4096, uint16_t, 4>(X, M, ld, mult, q, scale, st)
+              : launch_rq<4096, float, 4>(X, M, ld, mult, q, scale, st);
 }
 
 hipError_t launch_smooth_calibrate(const void* Xc, bool xbf16, int64_t Mc, int64_t ldx, const void* W, bool wbf16,

@@ -121,7 +121,9 @@ constexpr int waves_per_eu() {
   return (RB == 128 || (BN / WGN) * (BM / WGM) > 4096) ? 2 : (WGN * WGM == 8 ? 4 : 3);
 }
 
-template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias>
+// kW8: int8 operands (one code per byte, no widening, the accumulator is acc itself) instead of
+// packed int4.
+template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias, bool kW8>
 __global__ __launch_bounds__(64 * WGN * WGM)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB>()))) void w4a4_gemm_kernel(const uint8_t* __restrict__ Xq,
                                                             const float* __restrict__ x_scale,
@@ -133,9 +135,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB>()))) void 
   constexpr int kWaves = WGN * WGM, kThr = 64 * kWaves;
   constexpr int WN = BN / WGN, WM = BM / WGM;  // wave sub-tile
   constexpr int FN = WN / 32, FM = WM / 32;
-  constexpr int kRowBytes = RB;   // packed bytes of one tile row per stage (2 RB codes)
+  constexpr int kRowBytes = RB;   // bytes of one tile row per stage (2 RB int4 or RB int8 codes)
   constexpr int U = RB / 16;      // 16-byte units per tile row and stage
-  constexpr int kSub = RB / 16;   // K32 MFMA sub-steps per stage
+  constexpr int kSub = kW8 ? RB / 32 : RB / 16;  // K32 MFMA sub-steps per stage
   constexpr int kReads = RB / 32; // ds_read_b128 per fragment per stage
   constexpr int kUnits = (BN + BM) * U;  // 16-byte units per stage
   constexpr int kLoads = kUnits / kThr;                  // LDS-direct loads per lane per stage
@@ -161,7 +163,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB>()))) void 
   const int64_t tile_m = tile / tiles_n;
   const int64_t n0 = tile_n * BN;
   const int64_t m0 = tile_m * BM;
-  const int64_t row_bytes = K / 2;
+  const int64_t row_bytes = kW8 ? K : K / 2;  // bytes of one operand row
 
   // Source of each of this lane's loads; LDS unit P = 64 * (kWaves i + wave) + lane of the stage
   // buffer.
@@ -212,7 +214,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB>()))) void 
 
   const int r32 = lane & 31;
   const int h = lane >> 5;
-  const int nk = (int)(K / (2 * kRowBytes));
+  const int nk = (int)(kW8 ? K / kRowBytes : K / (2 * kRowBytes));
 
   // The tile's scales: scale slot i holds w_scale[n0 + i] (i < BN) or x_scale[m0 + i - BN] (rows
   // past M repeat the last row); thread t fetches slots t, t + kThr, ...  Issued before the stage
@@ -278,33 +280,46 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB>()))) void 
       for (int q = 0; q < kReads; ++q)
         pb[c][q] = *reinterpret_cast<const u32x4*>(Bs + r * kRowBytes + 16 * ((2 * q + h) ^ swz<U>(r)));
     }
-    // K32 sub-steps: sub-step s uses dwords 2(s&1), 2(s&1)+1 of read q = s >> 1.
+    if constexpr (kW8) {
+      // int8: read q is the whole MFMA operand of sub-step q (16 codes per lane, the other 16 of the
+      // K32 block in the lane 32 apart).
 #pragma unroll
-    for (int s = 0; s < kSub; ++s) {
-      v4i fa[FN];
+      for (int q = 0; q < kSub; ++q)
 #pragma unroll
-      for (int a = 0; a < FN; ++a) {
-        const uint32_t p0 = pa[a][s >> 1][2 * (s & 1)], p1 = pa[a][s >> 1][2 * (s & 1) + 1];
-        fa[a] = widen(p0, p1);
+        for (int c = 0; c < FM; ++c)
+#pragma unroll
+          for (int a = 0; a < FN; ++a)
+            acc[a][c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, pa[a][q]),
+                                                              __builtin_bit_cast(v4i, pb[c][q]), acc[a][c], 0, 0, 0);
+    } else {
+      // K32 sub-steps: sub-step s uses dwords 2(s&1), 2(s&1)+1 of read q = s >> 1.
+#pragma unroll
+      for (int s = 0; s < kSub; ++s) {
+        v4i fa[FN];
+#pragma unroll
+        for (int a = 0; a < FN; ++a) {
+          const uint32_t p0 = pa[a][s >> 1][2 * (s & 1)], p1 = pa[a][s >> 1][2 * (s & 1) + 1];
+          fa[a] = widen(p0, p1);
+        }
+#pragma unroll
+        for (int c = 0; c < FM; ++c) {
+          const uint32_t p0 = pb[c][s >> 1][2 * (s & 1)], p1 = pb[c][s >> 1][2 * (s & 1) + 1];
+          const v4i fb = widen(p0, p1);
+#pragma unroll
+          for (int a = 0; a < FN; ++a) acc[a][c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[a], fb, acc[a][c], 0, 0, 0);
+        }
       }
+      // Schedule: the fragment reads, the first sub-step's widening, then one MFMA per three VALU
+      // ops so the remaining widening overlaps the matrix core.
+      __builtin_amdgcn_sched_group_barrier(0x100, kReads * (FN + FM), 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6 * (FN + FM), 0);
 #pragma unroll
-      for (int c = 0; c < FM; ++c) {
-        const uint32_t p0 = pb[c][s >> 1][2 * (s & 1)], p1 = pb[c][s >> 1][2 * (s & 1) + 1];
-        const v4i fb = widen(p0, p1);
-#pragma unroll
-        for (int a = 0; a < FN; ++a) acc[a][c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[a], fb, acc[a][c], 0, 0, 0);
+      for (int i = 0; i < 2 * (kSub - 1) * (FN + FM); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, kSub * FN * FM - 2 * (kSub - 1) * (FN + FM), 0);
     }
-    // Schedule: the fragment reads, the first sub-step's widening, then one MFMA per three VALU
-    // ops so the remaining widening overlaps the matrix core.
-    __builtin_amdgcn_sched_group_barrier(0x100, kReads * (FN + FM), 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 6 * (FN + FM), 0);
-#pragma unroll
-    for (int i = 0; i < 2 * (kSub - 1) * (FN + FM); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kSub * FN * FM - 2 * (kSub - 1) * (FN + FM), 0);
     if constexpr (!QV_DMA) {
       // The buffer of stage kt + STAGES - 1 held stage kt - 1, which every wave finished reading
       // before this iteration's barrier.
@@ -342,12 +357,12 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB>()))) void 
     if constexpr (kFreeStaging) return ml * kOutRowBytes + 16 * (ch ^ (ml & 7));
     else return ml * kOutRowBytes + 16 * ch;
   };
-  // Row scales carry the 2^-8 of the accumulator (256 acc converts to fp32 exactly, |256 acc| <
-  // 2^26 with its low 8 bits zero); a row scale below 2^-118 becomes subnormal and keeps at least
-  // 16 significant bits.
+  // int4: row scales carry the 2^-8 of the accumulator (256 acc converts to fp32 exactly, |256 acc|
+  // < 2^26 with its low 8 bits zero); a row scale below 2^-118 becomes subnormal and keeps at least
+  // 16 significant bits.  int8: the accumulator is acc.
   float sa[FM];
 #pragma unroll
-  for (int c = 0; c < FM; ++c) sa[c] = scales[BN + wm * WM + 32 * c + r32] * 0.00390625f;
+  for (int c = 0; c < FM; ++c) sa[c] = scales[BN + wm * WM + 32 * c + r32] * (kW8 ? 1.0f : 0.00390625f);
 #pragma unroll
   for (int a = 0; a < FN; ++a) {
 #pragma unroll
@@ -400,7 +415,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB>()))) void 
   }
 }
 
-template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias>
+template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias, bool kW8>
 hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
                     int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
   constexpr size_t kLds = GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out>::kTotal;
@@ -409,13 +424,13 @@ hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
   if (!attr_set[dev]) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias>),
+        reinterpret_cast<const void*>(&w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias, kW8>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
     if (e != hipSuccess) return e;
     attr_set[dev] = 1;
   }
   const int64_t blocks = (N / BN) * ((M + BM - 1) / BM);
-  hipLaunchKernelGGL((w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias, kW8>), dim3((unsigned)blocks),
                      dim3(64 * WGN * WGM), kLds, st, Xq, xs, Wq, ws, bias, M, N, K, Y, ldy);
   return hipGetLastError();
 }
@@ -431,24 +446,25 @@ hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const
 #define QV_TILE_CFG 0
 #endif
 
-template <int BN, int BM, int WGN, int WGM, bool kBF16Out, bool kGelu, bool kBias>
+template <int BN, int BM, int WGN, int WGM, bool kBF16Out, bool kGelu, bool kBias, bool kW8>
 hipError_t launch_cfg(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
                       int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
   // 128 codes (64 bytes of every row) per stage; a 256-code stage variant is kept selectable for
   // measurements (it halves the barriers but its 64 KB ring leaves two blocks per CU).
-  if constexpr (QV_RB128) {
+  if constexpr (QV_RB128 && !kW8) {
     if ((K % 256) == 0)
-      return launch_t<BN, BM, WGN, WGM, 128, QV_STAGES_128, kBF16Out, kGelu, kBias>(Xq, xs, Wq, ws, bias, M, N, K, Y,
-                                                                                 ldy, st);
+      return launch_t<BN, BM, WGN, WGM, 128, QV_STAGES_128, kBF16Out, kGelu, kBias, kW8>(Xq, xs, Wq, ws, bias, M, N, K,
+                                                                                      Y, ldy, st);
   }
-  return launch_t<BN, BM, WGN, WGM, 64, QV_STAGES, kBF16Out, kGelu, kBias>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+  return launch_t<BN, BM, WGN, WGM, 64, QV_STAGES, kBF16Out, kGelu, kBias, kW8>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy,
+                                                                              st);
 }
 
-template <bool kBF16Out, bool kGelu, bool kBias>
+template <bool kBF16Out, bool kGelu, bool kBias, bool kW8>
 hipError_t launch_k(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
                     int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
 #define QV_LAUNCH(BN, BM, WGN, WGM) \
-  launch_cfg<BN, BM, WGN, WGM, kBF16Out, kGelu, kBias>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
+  launch_cfg<BN, BM, WGN, WGM, kBF16Out, kGelu, kBias, kW8>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
   if constexpr (!kBF16Out) {
     // fp32 outputs: the 256-wide tiles' output staging would not fit in LDS
     return QV_LAUNCH(128, 128, 2, 2);
@@ -467,23 +483,35 @@ hipError_t launch_k(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const
 
 }  // namespace
 
+namespace {
+
+template <bool kW8>
+hipError_t launch_gemm(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
+                       int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out, int64_t ldy,
+                       hipStream_t st) {
+#define QV_K(B, G, BIAS) launch_k<B, G, BIAS, kW8>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
+  if (bias) {
+    if (bf16_out) return gelu ? QV_K(true, true, true) : QV_K(true, false, true);
+    return gelu ? QV_K(false, true, true) : QV_K(false, false, true);
+  }
+  if (bf16_out) return gelu ? QV_K(true, true, false) : QV_K(true, false, false);
+  return gelu ? QV_K(false, true, false) : QV_K(false, false, false);
+#undef QV_K
+}
+
+}  // namespace
+
 hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws,
                             const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out,
                             int64_t ldy, hipStream_t st) {
-  if (bias) {
-    if (bf16_out) {
-      return gelu ? launch_k<true, true, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
-                  : launch_k<true, false, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
-    }
-    return gelu ? launch_k<false, true, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
-                : launch_k<false, false, true>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
-  }
-  if (bf16_out) {
-    return gelu ? launch_k<true, true, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
-                : launch_k<true, false, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
-  }
-  return gelu ? launch_k<false, true, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
-              : launch_k<false, false, false>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st);
+  return launch_gemm<false>(Xq, xs, Wq, ws, bias, M, N, K, gelu, Y, bf16_out, ldy, st);
+}
+
+hipError_t launch_w8a8_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
+                            const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out,
+                            int64_t ldy, hipStream_t st) {
+  return launch_gemm<true>(reinterpret_cast<const uint8_t*>(Xq), xs, reinterpret_cast<const uint8_t*>(Wq), ws, bias,
+                           M, N, K, gelu, Y, bf16_out, ldy, st);
 }
 
 }  // namespace qv

@@ -1,10 +1,11 @@
 """Device-resident state of a named workload and the two library calls of one online linear.
 
 A layer holds what the online step reads and writes: its input activations X (bf16 or fp32
-[M][K]), the activation-side smoothing multipliers 1/s ([K] fp32), the packed int4 weights and
-their per-channel scales (prepared once, offline), the code/scale buffers of the quantized
-activations and the output Y [M][N].  ``run_linear`` is the online path: rotate-smooth-quantize,
-then the int4 GEMM with its dequant (+GELU) epilogue, both on the given stream.
+[M][K]), the activation-side smoothing multipliers 1/s ([K] fp32), the quantized weights (packed
+int4, or int8 for the W8A8 variant) and their per-channel scales (prepared once, offline), the
+code/scale buffers of the quantized activations and the output Y [M][N].  ``run_linear`` is the
+online path: rotate-smooth-quantize, then the GEMM with its dequant (+GELU) epilogue, both on the
+given stream.
 
 Smoothing follows the method's calibration reading: the factors of a layer come from the first
 frame (1374 rows) of that layer's own input activations and from its weights.  In the MLP chain
@@ -24,11 +25,12 @@ class Layer:
     block: int
     X: object      # [M][K] activations (None until a chain links it)
     inv: object    # [K] fp32, 1 / smoothing factor
-    Wq: object     # [N][K/2] uint8 packed int4 weights
+    Wq: object     # [N][K/2] uint8 packed int4 (or [N][K] int8) weight codes
     ws: object     # [N] fp32 weight scales
-    Xq: object     # [M][K/2] uint8 packed int4 activation codes
+    Xq: object     # [M][K/2] uint8 packed int4 (or [M][K] int8) activation codes
     xs: object     # [M] fp32 activation scales
     Y: object      # [M][N] output
+    bits: int = 4  # 4: packed int4 codes (W4A4); 8: int8 codes (W8A8)
 
 
 def torch_dtype(name: str):
@@ -45,30 +47,37 @@ def seeds(wl: Workload, lin: Linear, block: int):
 
 
 def run_linear(qv, L: Layer, stream=None) -> None:
-    """The online W4A4 linear: qv_hadamard_smooth_quant, then qv_w4a4_gemm."""
-    qv.qv_hadamard_smooth_quant(L.X, L.inv, L.Xq, L.xs, stream)
-    qv.qv_w4a4_gemm(L.Xq, L.xs, L.Wq, L.ws, None, L.Y, L.lin.epi, stream)
+    """The online linear: rotate-smooth-quantize, then the GEMM with its epilogue (W4A4 or W8A8)."""
+    if L.bits == 8:
+        qv.qv_hadamard_smooth_quant8(L.X, L.inv, L.Xq, L.xs, stream)
+        qv.qv_w8a8_gemm(L.Xq, L.xs, L.Wq, L.ws, None, L.Y, L.lin.epi, stream)
+    else:
+        qv.qv_hadamard_smooth_quant(L.X, L.inv, L.Xq, L.xs, stream)
+        qv.qv_w4a4_gemm(L.Xq, L.xs, L.Wq, L.ws, None, L.Y, L.lin.epi, stream)
 
 
-def build(qv, wl: Workload, device, share_outputs: bool = False):
+def build(qv, wl: Workload, device, share_outputs: bool = False, bits: int = 4):
     """Allocate and prepare every layer of ``wl`` on ``device`` (timing inputs, seeded on device).
 
     Activations are drawn per layer and per block.  With ``share_outputs`` the code/scale buffers
     and outputs are shared by the layers of equal shape across blocks (a 48-block stack would
     otherwise hold 48 copies of buffers that each step overwrites in order).  Weights are packed
-    with ``qv_pack_weights`` after ``qv_smooth_calibrate`` on frame 0 of the layer's input.
+    with ``qv_pack_weights`` (``qv_pack_weights8`` for ``bits=8``) after ``qv_smooth_calibrate`` on
+    frame 0 of the layer's input.
     """
     import torch
 
     M = wl.M
     in_dt, out_dt = torch_dtype(wl.in_dtype), torch_dtype(wl.out_dtype)
+    code_dt = torch.int8 if bits == 8 else torch.uint8
+    row_codes = (lambda K: K) if bits == 8 else (lambda K: K // 2)
     shared = {}
 
     def buffers(lin):
         key = (lin.name, lin.K, lin.N)
         if share_outputs and key in shared:
             return shared[key]
-        b = (torch.empty((M, lin.K // 2), dtype=torch.uint8, device=device),
+        b = (torch.empty((M, row_codes(lin.K)), dtype=code_dt, device=device),
              torch.empty((M,), dtype=torch.float32, device=device),
              torch.empty((M, lin.N), dtype=out_dt, device=device))
         shared[key] = b
@@ -89,12 +98,12 @@ def build(qv, wl: Workload, device, share_outputs: bool = False):
             else:
                 calib = X[:synth.FRAME_TOKENS]
             qv.qv_smooth_calibrate(calib, W, s, inv, 0.5)
-            Wq = torch.empty((lin.N, lin.K // 2), dtype=torch.uint8, device=device)
+            Wq = torch.empty((lin.N, row_codes(lin.K)), dtype=code_dt, device=device)
             ws = torch.empty((lin.N,), dtype=torch.float32, device=device)
-            qv.qv_pack_weights(W, s, Wq, ws)
+            (qv.qv_pack_weights8 if bits == 8 else qv.qv_pack_weights)(W, s, Wq, ws)
             del W
             Xq, xs, Y = buffers(lin)
-            L = Layer(lin, blk, X, inv, Wq, ws, Xq, xs, Y)
+            L = Layer(lin, blk, X, inv, Wq, ws, Xq, xs, Y, bits)
             if chained:
                 L.X = prev.Y
             layers.append(L)
@@ -109,8 +118,8 @@ def frame0_output(qv, L: Layer, device):
 
     F = min(synth.FRAME_TOKENS, L.X.shape[0])
     tmp = Layer(L.lin, L.block, L.X[:F], L.inv, L.Wq, L.ws,
-                torch.empty((F, L.lin.K // 2), dtype=torch.uint8, device=device),
+                torch.empty((F, L.Xq.shape[1]), dtype=L.Xq.dtype, device=device),
                 torch.empty((F,), dtype=torch.float32, device=device),
-                torch.empty((F, L.lin.N), dtype=L.Y.dtype, device=device))
+                torch.empty((F, L.lin.N), dtype=L.Y.dtype, device=device), L.bits)
     run_linear(qv, tmp)
     return tmp.Y

@@ -1,6 +1,6 @@
 /*
  * qv.h -- C ABI of libqv, an MI355X (gfx950) library for the W4A4 Hadamard-rotated, smoothed,
- * int4-quantized linear layer of QuantVGGT.
+ * int4-quantized linear layer of QuantVGGT (and its W8A8 variant, at the end of this file).
  *
  * Sources, cited by page title and section:
  *   [P4] "十亿参数的三维重建模型，能塞进手机吗？" (gslzct.com), a translation of the QuantVGGT
@@ -54,7 +54,7 @@ typedef enum {
   QV_ERR_UNSUPPORTED = 3, /* the request is well formed but outside what the kernels implement */
   QV_ERR_ALIGN = 4,       /* a pointer or row stride is not 16-byte aligned */
   QV_ERR_DTYPE = 5,       /* unknown dtype or epilogue value */
-  QV_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than qv_w4a4_linear_workspace_size() */
+  QV_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the matching *_linear_workspace_size() */
   QV_ERR_HIP = 7,         /* the HIP runtime reported an error when launching */
   QV_ERR_INTERNAL = 8     /* an unexpected internal error */
 } qv_status;
@@ -131,6 +131,40 @@ qv_status qv_w4a4_linear(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, 
 qv_status qv_smooth_calibrate(const void* Xc, qv_dtype xc_dtype, int64_t Mc, int64_t ldx, const void* W,
                               qv_dtype w_dtype, int64_t N, int64_t ldw, int64_t K, float alpha,
                               float* smooth, float* inv_smooth, void* hip_stream);
+
+/*
+ * W8A8: the pages' second setting ([P3]: W8A8 next to W4A4;  [P4] 训练后量化（PTQ） with N = 8).
+ * The same rotation, smoothing and per-token / per-output-channel scales, with
+ *   scale = max |Xt| / 127,  q = clamp(rne(Xt / scale), -128, 127),
+ * one two's-complement int8 code per byte, row-major, K bytes per row (Xq8, Wq8).
+ *
+ * qv_hadamard_smooth_quant8 / qv_pack_weights8 -- as qv_hadamard_smooth_quant / qv_pack_weights
+ *   (same arguments and rules), writing int8 codes [M][K] / [N][K].
+ */
+qv_status qv_hadamard_smooth_quant8(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                    const float* inv_smooth, int8_t* Xq8, float* x_scale, void* hip_stream);
+qv_status qv_pack_weights8(const void* W, qv_dtype w_dtype, int64_t N, int64_t K, int64_t ldw,
+                           const float* smooth, int8_t* Wq8, float* w_scale, void* hip_stream);
+
+/*
+ * qv_w8a8_gemm -- int8 x int8 contraction (int32 accumulation, exact) with the epilogue of
+ * qv_w4a4_gemm.  Xq8 [M][K], Wq8 [N][K] int8;  K a multiple of 64 in [64, 65536];  N a multiple of
+ * 128;  other arguments and rules as for qv_w4a4_gemm.
+ */
+qv_status qv_w8a8_gemm(const int8_t* Xq8, const float* x_scale, const int8_t* Wq8, const float* w_scale,
+                       const float* bias, int64_t M, int64_t N, int64_t K, qv_epilogue epi, void* Y,
+                       qv_dtype y_dtype, int64_t ldy, void* hip_stream);
+
+/* Workspace of qv_w8a8_linear: M*K code bytes and 4*M scale bytes, each rounded up to 256 bytes
+ * (0 for invalid sizes). */
+size_t qv_w8a8_linear_workspace_size(int64_t M, int64_t K);
+
+/* qv_w8a8_linear -- qv_hadamard_smooth_quant8 into the workspace, then qv_w8a8_gemm; arguments and
+ * workspace rules as for qv_w4a4_linear. */
+qv_status qv_w8a8_linear(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, int64_t ldx,
+                         const float* inv_smooth, const int8_t* Wq8, const float* w_scale,
+                         const float* bias, int64_t N, qv_epilogue epi, void* Y, qv_dtype y_dtype,
+                         int64_t ldy, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 #ifdef __cplusplus
 }

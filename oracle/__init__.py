@@ -211,3 +211,24 @@ def w4a4_linear(X, inv_smooth, Wq, w_scale, bias=None, epi: int = 0, mode: int =
     _check(lib().qvref_w4a4_linear(_p(X), M, K, K, _p(inv_smooth), _p(Wq), _p(ws), _p(bias), N, epi,
                                    mode, _p(Y)), "w4a4_linear")
     return Y
+
+
+# ---------------------------------------------------------------- W8A8 ([P4] 训练后量化（PTQ）, N = 8)
+# The pages' second setting: the same rotation and smoothing, codes in [-128, 127] with scale
+# absmax / 127, one int8 code per element (no packing).  Composed from the primitives above.
+
+def hadamard_smooth_quant8(X, inv_smooth=None, mode: int = ROT_EXPLICIT):
+    """Oracle of the 8-bit activation step: returns (Xq8 [M, K] int8, x_scale [M] fp32)."""
+    return quantize_rows(rotate(X, mode), inv_smooth, bits=8)
+
+
+def pack_weights8(W, smooth=None, mode: int = ROT_EXPLICIT):
+    """Oracle of the 8-bit weight step: returns (Wq8 [N, K] int8, w_scale [N] fp32)."""
+    return quantize_rows(rotate(W, mode), smooth, bits=8)
+
+
+def w8a8_gemm(Xq8, x_scale, Wq8, w_scale, bias=None, epi: int = 0, return_acc: bool = False):
+    """acc = Xq8 . Wq8^T (exact), Y = dequant(acc) (+ bias) (+ GELU)."""
+    acc = gemm_int(Xq8, Wq8)
+    Y = dequant(acc, x_scale, w_scale, bias, epi)
+    return (Y, acc) if return_acc else Y

@@ -31,7 +31,7 @@ CODE_MISMATCH_MAX = 1e-4
 OUT_REL_MAX = 1e-3
 
 
-def code_bounds(X, mult, Xhat=None, dX=None):
+def code_bounds(X, mult, Xhat=None, dX=None, qmax: int = 7):
     """Exact code-space values t and the per-element tolerance tau for rows X (fp32 values).
 
     ``dX`` (optional, same shape) bounds how far the GPU's input rows may differ from X elementwise
@@ -45,9 +45,9 @@ def code_bounds(X, mult, Xhat=None, dX=None):
     L = math.log2(K)
     xt = Xhat * m
     a = np.max(np.abs(xt), axis=1)
-    s = a / 7.0
+    s = a / float(qmax)
     # Rows whose fp32 scale is zero or subnormal quantize to all-zero codes on both sides.
-    flushed = (np.max(np.abs(Xhat.astype(np.float32) * m.astype(np.float32)), axis=1) / np.float32(7)) < FLT_MIN32
+    flushed = (np.max(np.abs(Xhat.astype(np.float32) * m.astype(np.float32)), axis=1) / np.float32(qmax)) < FLT_MIN32
     s = np.where(flushed, 0.0, s)
     with np.errstate(divide="ignore", invalid="ignore"):
         t = np.where(s[:, None] > 0, xt / s[:, None], 0.0)
@@ -61,12 +61,12 @@ def code_bounds(X, mult, Xhat=None, dX=None):
     return t, tau, s, rel_scale
 
 
-def check_codes(q_gpu, q_ref, t, tau, label=""):
+def check_codes(q_gpu, q_ref, t, tau, label="", qmax: int = 7):
     """Every GPU code admissible; mismatch rate <= 1e-4.  Returns the mismatch rate."""
     q_gpu = np.asarray(q_gpu, dtype=np.int64)
     q_ref = np.asarray(q_ref, dtype=np.int64)
-    lo = np.clip(np.rint(t - tau), -8, 7)
-    hi = np.clip(np.rint(t + tau), -8, 7)
+    lo = np.clip(np.rint(t - tau), -qmax - 1, qmax)
+    hi = np.clip(np.rint(t + tau), -qmax - 1, qmax)
     bad = (q_gpu < lo) | (q_gpu > hi)
     if np.any(bad):
         idx = np.argwhere(bad)[:5]

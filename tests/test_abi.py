@@ -145,3 +145,30 @@ def test_binding_raises_on_error_status(L):
     with pytest.raises(qv.QVError) as e:
         qv._check(QV_ERR_SHAPE, "probe")
     assert "QV_ERR_SHAPE" in str(e.value)
+
+
+def test_w8a8_argument_errors(L):
+    import bit_ptq_reconstruction_amd as qv
+
+    assert qv.qv_w8a8_linear_workspace_size(1374, 1024) == 1374 * 1024 + ((1374 * 4 + 255) // 256) * 256
+    assert qv.qv_w8a8_linear_workspace_size(-1, 1024) == 0
+    # rotate-quantize to int8: the same rules as the int4 step
+    assert L.qv_hadamard_smooth_quant8(P, 0, 0, 1024, 1024, None, P, P, None) == QV_OK
+    assert L.qv_hadamard_smooth_quant8(P, 0, 16, 2048, 2048, None, P, P, None) == QV_ERR_UNSUPPORTED
+    assert L.qv_hadamard_smooth_quant8(P, 0, 16, 1024, 1024, None, None, P, None) == QV_ERR_NULL
+    assert L.qv_hadamard_smooth_quant8(P, 0, 16, 1024, 1024, None, P_MIS, P, None) == QV_ERR_ALIGN
+    assert L.qv_pack_weights8(P, 0, 8, 4096, 4095, None, P, P, None) == QV_ERR_SHAPE
+
+    def g8(K=1024, N=128, ldy=128, Xq=P, **kw):
+        return L.qv_w8a8_gemm(Xq, P, P, P, None, 16, N, K, kw.get("epi", 0), P, 0, ldy, None)
+
+    # K = 192 passes the K rule (int8 operands step K by 64): the call fails later, on the NULL pointer
+    assert g8(K=64 * 3, Xq=None) == QV_ERR_NULL
+    assert g8(K=100) == QV_ERR_UNSUPPORTED
+    assert g8(K=65536 + 64) == QV_ERR_UNSUPPORTED
+    assert g8(N=64, ldy=64) == QV_ERR_UNSUPPORTED
+    assert g8(Xq=None) == QV_ERR_NULL
+    assert g8(epi=5) == QV_ERR_DTYPE
+    need = L.qv_w8a8_linear_workspace_size(16, 1024)
+    assert L.qv_w8a8_linear(P, 0, 16, 1024, 1024, None, P, P, None, 128, 0, P, 0, 128, P, need - 1, None) == \
+        QV_ERR_WORKSPACE

@@ -164,6 +164,28 @@ def test_quantizer_8bit_range(oracle_mod):
     assert np.max(np.abs(q)) == 127
 
 
+def test_quantizer_8bit_constructed_ties_and_error_bound(oracle_mod):
+    """8-bit codes ([P4] 训练后量化（PTQ） with N = 8): rows x = t H / sqrt(d) built from half-integer
+    targets t with max |t| = 127 rotate back to t exactly (integer sums, exact in fp64 and fp32), so
+    the scale is 1 and every code is t rounded half to even (numpy's rint, an independent rounding);
+    on random rows every code stays within half a step of its value."""
+    d = 256
+    rng = np.random.default_rng(21)
+    t = rng.integers(-254, 255, size=(3, d)).astype(np.float64) / 2.0
+    t[:, 0] = [127.0, -127.0, 127.0]
+    t[2, 1:9] = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, -126.5]
+    H = O.hadamard(d).astype(np.float64)
+    X = t @ H / np.sqrt(d)
+    q, s = O.hadamard_smooth_quant8(X)
+    assert np.all(s == np.float32(1.0))
+    np.testing.assert_array_equal(q, np.rint(t).astype(np.int8))
+    Xr = synth.vggt_activations(6, 1024, seed=22)
+    q, s = O.hadamard_smooth_quant8(Xr, mode=O.ROT_FWHT)
+    Xh = O.rotate(Xr, O.ROT_FWHT)
+    assert np.all(np.abs(Xh - q * s[:, None].astype(np.float64)) <= s[:, None] * (0.5 + 1e-5))
+    assert np.all(np.abs(q).max(axis=1) == 127)
+
+
 def test_quantizer_multiplier_applies_per_channel(oracle_mod):
     Xh = np.ones((1, 8)) * np.arange(1, 9)
     mult = np.array([1, 1, 1, 1, 1, 1, 1, 0.5], dtype=np.float32)
