@@ -44,7 +44,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #ifndef QV_STAGES
-#define QV_STAGES 3  // LDS ring depth of the GEMM main loop, 128 codes per stage
+#define QV_STAGES 2  // LDS ring depth of the GEMM main loop, 128 int4 codes per stage
 #endif
 #ifndef QV_RB128
 #define QV_RB128 0
@@ -114,18 +114,20 @@ struct GemmLds {
   static constexpr size_t kTotal = kScaleOffset + 4 * (size_t)(BN + BM);
 };
 
-// Waves per SIMD the register allocation must allow: three 4-wave blocks of 64 x 64 wave tiles per
-// CU; two waves per SIMD for the larger wave tiles (128 accumulator registers each).
-template <int BN, int BM, int WGN, int WGM, int RB>
+// Waves per SIMD the register allocation must allow (at most 128 registers per lane for 4):
+// 64 x 64 wave tiles with a 2-deep ring of 64-byte stages fit four 4-wave or two 8-wave blocks per
+// CU; a 3-deep ring leaves room for three 4-wave blocks; the 128-accumulator wave tiles and the
+// 128-byte stages allow two.
+template <int BN, int BM, int WGN, int WGM, int RB, int STAGES>
 constexpr int waves_per_eu() {
-  return (RB == 128 || (BN / WGN) * (BM / WGM) > 4096) ? 2 : (WGN * WGM == 8 ? 4 : 3);
+  return (RB == 128 || (BN / WGN) * (BM / WGM) > 4096) ? 2 : ((WGN * WGM == 8 || STAGES == 2) ? 4 : 3);
 }
 
 // kW8: int8 operands (one code per byte, no widening, the accumulator is acc itself) instead of
 // packed int4.
 template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias, bool kW8>
 __global__ __launch_bounds__(64 * WGN * WGM)
-__attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB>()))) void w4a4_gemm_kernel(const uint8_t* __restrict__ Xq,
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES>()))) void w4a4_gemm_kernel(const uint8_t* __restrict__ Xq,
                                                             const float* __restrict__ x_scale,
                                                             const uint8_t* __restrict__ Wq,
                                                             const float* __restrict__ w_scale,
@@ -333,84 +335,114 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB>()))) void 
   // by 8 or 16 bytes so the staging writes spread over the banks); the block is then written with
   // 16-byte non-temporal stores, each group of lanes covering whole contiguous row segments.
   using OutT = typename std::conditional<kBF16Out, uint16_t, float>::type;
-  // Staging without a block barrier: after the last stage's barrier no wave reads any ring buffer
-  // but the last stage's, and every LDS-DMA has landed, so the other STAGES - 1 buffers are free.
-  // When the wave blocks fit there (two waves per 16 KB buffer for 128 x 128 bf16 tiles), each wave
-  // stages at once, in rows of exactly WN outputs whose 16-byte chunks are XOR-swizzled by the row;
-  // otherwise the block synchronizes and stages over the whole ring with padded rows.
-  constexpr int kWaveOutBytes = WM * WN * (int)sizeof(OutT);
-  constexpr bool kFreeStaging = STAGES >= 3 && kStageBytes % kWaveOutBytes == 0 &&
-                                kWaves <= (STAGES - 1) * (kStageBytes / kWaveOutBytes) && WN * (int)sizeof(OutT) == 128;
-  constexpr int kOutRowBytes = WN * (int)sizeof(OutT) + (kFreeStaging ? 0 : (kBF16Out ? 8 : 16));
-  uint8_t* stage_out;
-  if constexpr (kFreeStaging) {
-    constexpr int kPerBuf = kStageBytes / kWaveOutBytes;  // wave blocks per free buffer
-    const int slot = wave / kPerBuf;                      // index among the free buffers
-    const int buf = (nk + slot) % STAGES;                 // skips (nk - 1) % STAGES, the last stage
-    stage_out = lds + buf * kStageBytes + (wave % kPerBuf) * kWaveOutBytes;
-  } else {
-    __syncthreads();  // every wave is done with the stage buffers
-    stage_out = lds + wave * (WM * kOutRowBytes);
-  }
-  // Byte offset of the 16-byte chunk ch of row ml in the staging block.
-  auto chunk_at = [&](int ml, int ch) {
-    if constexpr (kFreeStaging) return ml * kOutRowBytes + 16 * (ch ^ (ml & 7));
-    else return ml * kOutRowBytes + 16 * ch;
-  };
   // int4: row scales carry the 2^-8 of the accumulator (256 acc converts to fp32 exactly, |256 acc|
   // < 2^26 with its low 8 bits zero); a row scale below 2^-118 becomes subnormal and keeps at least
   // 16 significant bits.  int8: the accumulator is acc.
   float sa[FM];
 #pragma unroll
   for (int c = 0; c < FM; ++c) sa[c] = scales[BN + wm * WM + 32 * c + r32] * (kW8 ? 1.0f : 0.00390625f);
+  // y for fragment (a, c) and register group vg: the lane's four consecutive columns
+  // n = wn*WN + 32a + 8vg + 4h + (0..3) of row m = wm*WM + 32c + r32, dequantized (+ bias) (+ GELU).
+  auto outputs = [&](int a, int c, int vg, float (&y)[4]) {
+    const int nl = 32 * a + 8 * vg + 4 * h;
+    const float4 sw4 = *reinterpret_cast<const float4*>(scales + wn * WN + nl);
+    const float sw[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
+    float bb[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kBias) {
+      const float4 b4 = *reinterpret_cast<const float4*>(bias + n0 + wn * WN + nl);
+      bb[0] = b4.x; bb[1] = b4.y; bb[2] = b4.z; bb[3] = b4.w;
+    }
 #pragma unroll
-  for (int a = 0; a < FN; ++a) {
+    for (int v = 0; v < 4; ++v) {
+      y[v] = (float)acc[a][c][4 * vg + v] * sa[c] * sw[v];
+      if constexpr (kBias) y[v] += bb[v];
+      if constexpr (kGelu) y[v] = gelu(y[v]);
+    }
+  };
+  constexpr int kChunksPerRow = WN * (int)sizeof(OutT) / 16;  // 16-byte chunks per row
+  constexpr int kRowsPerPass = 64 / kChunksPerRow;            // rows one wave-wide read covers
+
+  // bf16 outputs are staged without a block barrier: after the last stage's barrier no wave reads
+  // any ring buffer but the last stage's (every LDS-DMA has landed, no refill follows), so buffer
+  // nk % STAGES is free.  Each wave stages its block in 32-row passes (one fragment row c at a
+  // time) through a 4 KB slice of that buffer, rows of exactly WN outputs with 16-byte chunks
+  // XOR-swizzled by the row.  Other blocks synchronize and stage over the whole ring, rows padded.
+  constexpr int kPassBytes = 32 * WN * (int)sizeof(OutT);
+  constexpr bool kFreeStaging = kBF16Out && WN * (int)sizeof(OutT) == 128 && kWaves * kPassBytes <= kStageBytes;
+  if constexpr (kFreeStaging) {
+    uint8_t* const stage_out = lds + (nk % STAGES) * kStageBytes + wave * kPassBytes;
 #pragma unroll
-    for (int vg = 0; vg < 4; ++vg) {
-      const int nl = 32 * a + 8 * vg + 4 * h;  // column inside the wave block
-      const float4 sw4 = *reinterpret_cast<const float4*>(scales + wn * WN + nl);
-      const float sw[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
-      float bb[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (kBias) {
-        const float4 b4 = *reinterpret_cast<const float4*>(bias + n0 + wn * WN + nl);
-        bb[0] = b4.x; bb[1] = b4.y; bb[2] = b4.z; bb[3] = b4.w;
-      }
+    for (int c = 0; c < FM; ++c) {
 #pragma unroll
-      for (int c = 0; c < FM; ++c) {
-        const int ml = 32 * c + r32;  // row inside the wave block
-        float y[4];
+      for (int a = 0; a < FN; ++a) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          y[v] = (float)acc[a][c][4 * vg + v] * sa[c] * sw[v];
-          if constexpr (kBias) y[v] += bb[v];
-          if constexpr (kGelu) y[v] = gelu(y[v]);
-        }
-        uint8_t* dst = stage_out + chunk_at(ml, nl * (int)sizeof(OutT) / 16) + (nl * (int)sizeof(OutT)) % 16;
-        if constexpr (kBF16Out) {
+        for (int vg = 0; vg < 4; ++vg) {
+          float y[4];
+          outputs(a, c, vg, y);
           const bf16x2 lo = __builtin_convertvector((f32x2{y[0], y[1]}), bf16x2);
           const bf16x2 hi = __builtin_convertvector((f32x2{y[2], y[3]}), bf16x2);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-        } else {
-          *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+          // row r32, chunk 4a + vg swizzled by the row, half h of the chunk
+          *reinterpret_cast<uint2*>(stage_out + r32 * 128 + 16 * ((4 * a + vg) ^ (r32 & 7)) + 8 * h) =
+              make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // wave-local: read back by this wave
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int pass = 0; pass < 32 / kRowsPerPass; ++pass) {
+        const int ml = pass * kRowsPerPass + lane / kChunksPerRow;
+        const int ch = lane % kChunksPerRow;
+        const int64_t m = m0 + wm * WM + 32 * c + ml;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage_out + ml * 128 + 16 * (ch ^ (ml & 7)));
+        if (m < M) {
+          uint8_t* out = reinterpret_cast<uint8_t*>(static_cast<OutT*>(Y) + m * ldy + n0 + wn * WN) + 16 * ch;
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out));
+        }
+      }
+      // the next pass rewrites this slice after the reads above
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  } else {
+    constexpr int kOutRowBytes = WN * (int)sizeof(OutT) + (kBF16Out ? 8 : 16);
+    __syncthreads();  // every wave is done with the stage buffers
+    uint8_t* const stage_out = lds + wave * (WM * kOutRowBytes);
+#pragma unroll
+    for (int a = 0; a < FN; ++a) {
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+#pragma unroll
+        for (int c = 0; c < FM; ++c) {
+          float y[4];
+          outputs(a, c, vg, y);
+          const int nl = 32 * a + 8 * vg + 4 * h;
+          uint8_t* dst = stage_out + (32 * c + r32) * kOutRowBytes + nl * (int)sizeof(OutT);
+          if constexpr (kBF16Out) {
+            const bf16x2 lo = __builtin_convertvector((f32x2{y[0], y[1]}), bf16x2);
+            const bf16x2 hi = __builtin_convertvector((f32x2{y[2], y[3]}), bf16x2);
+            *reinterpret_cast<uint2*>(dst) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+          } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+          }
         }
       }
     }
-  }
-  // Wave-local: the block written above is read back by the same wave only.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  constexpr int kChunksPerRow = WN * (int)sizeof(OutT) / 16;  // 16-byte chunks per row
-  constexpr int kRowsPerPass = 64 / kChunksPerRow;
+    // Wave-local: the block written above is read back by the same wave only.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-  for (int pass = 0; pass < WM / kRowsPerPass; ++pass) {
-    const int ml = pass * kRowsPerPass + lane / kChunksPerRow;
-    const int ch = lane % kChunksPerRow;
-    const int64_t m = m0 + wm * WM + ml;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(stage_out + chunk_at(ml, ch));
-    if (m < M) {
-      uint8_t* out = reinterpret_cast<uint8_t*>(static_cast<OutT*>(Y) + m * ldy + n0 + wn * WN) + 16 * ch;
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out));
+    for (int pass = 0; pass < WM / kRowsPerPass; ++pass) {
+      const int ml = pass * kRowsPerPass + lane / kChunksPerRow;
+      const int ch = lane % kChunksPerRow;
+      const int64_t m = m0 + wm * WM + ml;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage_out + ml * kOutRowBytes + 16 * ch);
+      if (m < M) {
+        uint8_t* out = reinterpret_cast<uint8_t*>(static_cast<OutT*>(Y) + m * ldy + n0 + wn * WN) + 16 * ch;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out));
+      }
     }
   }
 }
