@@ -58,6 +58,32 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kXcds = 8;
 
+// Position inside an XCD's run -> offset in the run's canonical (row-major over tiles) order.
+// G = 0 keeps the canonical order: the blocks in flight share a few activation rows and sweep every
+// weight tile, which suits weights that stay in L2.  G > 0 walks each chunk of G tile rows column by
+// column, so the blocks in flight cover G activation rows and a few weight tiles, and each weight
+// tile is fetched once per chunk; a last chunk of fewer whole rows is transposed the same way and any
+// final partial row keeps the canonical order.
+__device__ __forceinline__ int64_t run_offset(int64_t local, int64_t cnt, int64_t tiles_n, int64_t G) {
+  if (G == 0) return local;
+  const int64_t chunk = G * tiles_n;
+  const int64_t c0 = (local / chunk) * chunk;
+  const int64_t rows = (cnt - c0 < chunk ? cnt - c0 : chunk) / tiles_n;  // whole rows in this chunk
+  const int64_t j = local - c0;
+  if (j >= rows * tiles_n) return local;  // partial last row
+  return c0 + (j % rows) * tiles_n + j / rows;
+}
+
+// Tile rows per chunk of run_offset.  int4 weights (2 MB for the widest layer) stay in an XCD's
+// 4 MB L2 in the canonical order.  A 4096 x 1024 int8 weight fills it, and is re-fetched for every
+// few activation rows unless chunks of 16 rows (16 activation tiles of 128 x 1024 bytes, 2 MB)
+// bound the sweep.  With 4096-byte rows 16 activation tiles no longer fit either, and the canonical
+// order, which reuses the activation tile, fetches less.
+template <bool kW8>
+__device__ __forceinline__ int64_t chunk_rows(int64_t tile_bytes) {
+  return (kW8 && 16 * tile_bytes <= (2 << 20)) ? 16 : 0;
+}
+
 // XOR swizzle of the 16-byte units of a tile row (U units per row): conflict-free fragment reads
 // whether the LDS serves 8 lanes per 128 bytes or 16 lanes per 256 bytes.
 template <int U>
@@ -160,7 +186,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES>())
   const int64_t b = blockIdx.x;
   const int64_t per = tiles / kXcds, rem = tiles % kXcds;
   const int64_t xcd = b % kXcds, local = b / kXcds;
-  const int64_t tile = xcd * per + (xcd < rem ? xcd : rem) + local;
+  const int64_t cnt = per + (xcd < rem ? 1 : 0);
+  const int64_t tile = xcd * per + (xcd < rem ? xcd : rem) +
+                       run_offset(local, cnt, tiles_n, chunk_rows<kW8>(BM * (kW8 ? K : K / 2)));
   const int64_t tile_n = tile % tiles_n;
   const int64_t tile_m = tile / tiles_n;
   const int64_t n0 = tile_n * BN;
