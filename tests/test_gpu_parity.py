@@ -197,6 +197,26 @@ def test_gemm_tiny_row_scales(qv, dev):
         acc.check_outputs(Y, Y_ref, False, f"tiny row scales epi={epi}")
 
 
+@pytest.mark.parametrize("out", ["fp32", "bf16"])
+def test_gelu_epilogue_sweep(qv, dev, out):
+    """The GELU epilogue over y in [-13.9, 10.4], out to the tail where fp32 outputs turn subnormal:
+    every accumulator is 1 (one code pair of 1 at k = 0), so y = x_scale[m] w_scale[n] spans a dense
+    grid.  fp32 outputs (degree-5 fit) must stay within 1e-4 relative, bf16 outputs within 1 ulp."""
+    M, N, K = 4096, 256, 128
+    Xq = np.zeros((M, K // 2), dtype=np.uint8)
+    Wq = np.zeros((N, K // 2), dtype=np.uint8)
+    Xq[:, 0] = 1
+    Wq[:, 0] = 1
+    xs = np.linspace(-13.4, 10.0, M).astype(np.float32)
+    ws = (1.0 + np.arange(N) * (0.04 / N)).astype(np.float32)
+    Y = run_gemm(qv, dev, Xq, xs, Wq, ws, None, 1, out)
+    Y_ref = oracle.w4a4_gemm(Xq, xs, Wq, ws, None, 1)
+    worst = acc.check_outputs(Y, Y_ref, out == "bf16", f"GELU sweep ({out})")
+    if out == "fp32":
+        assert worst <= 1e-4, f"GELU sweep: max relative error {worst:.2e}"
+    print(f"GELU sweep {out}: worst {worst:.2e} ({'bf16 ulps' if out == 'bf16' else 'relative'})")
+
+
 @pytest.mark.parametrize("K,epi,bias", [(256, 0, False), (256, 1, True), (1024, 0, False)])
 def test_gemm_many_tiles_per_block(qv, dev, K, epi, bias):
     """bf16 outputs over more tiles than resident blocks (each block walks several tiles, its LDS ring
