@@ -55,6 +55,7 @@ def lib():
             "qvref_pack_weights": [P, i64, i64, i64, P, i32, P, P],
             "qvref_w4a4_gemm": [P, P, P, P, P, i64, i64, i64, i32, P, P],
             "qvref_w4a4_linear": [P, i64, i64, i64, P, P, P, P, i64, i32, i32, P],
+            "qvref_dequant_grouped": [P, P, P, P, P, i64, i64, i64, i64, i32, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -232,3 +233,58 @@ def w8a8_gemm(Xq8, x_scale, Wq8, w_scale, bias=None, epi: int = 0, return_acc: b
     acc = gemm_int(Xq8, Wq8)
     Y = dequant(acc, x_scale, w_scale, bias, epi)
     return (Y, acc) if return_acc else Y
+
+
+# ------------------------------------------------ group-wise granularity ([P4] 细粒度量化粒度)
+# The subsection is truncated on the page.  Reading: the rotation and smoothing stay as above
+# (pre-global, over the whole row); each row of activations and of weights is then quantized in
+# groups of `group` consecutive channels, each group with its own symmetric scale absmax / 7, and
+# the product sums the groups' integer dot products dequantized by their own pair of scales.
+# The quantizer is the per-row one applied to each group's slice of the row.
+
+def quantize_groups(Xhat, mult=None, group: int = 128, bits: int = 4):
+    """Symmetric quantization per (row, group of channels); returns (q [R, K], scale [R, K/group])."""
+    Xhat = _f64(Xhat)
+    R, K = Xhat.shape
+    if group <= 0 or K % group:
+        raise ValueError("group must divide K")
+    mult = None if mult is None else np.asarray(mult, dtype=np.float32)
+    q = np.empty((R, K), dtype=np.int8)
+    s = np.empty((R, K // group), dtype=np.float32)
+    for g in range(K // group):
+        sl = slice(g * group, (g + 1) * group)
+        q[:, sl], s[:, g] = quantize_rows(Xhat[:, sl], None if mult is None else mult[sl], bits)
+    return q, s
+
+
+def hadamard_smooth_quant_grouped(X, inv_smooth=None, group: int = 128, mode: int = ROT_EXPLICIT):
+    """Grouped activation step: returns (Xq packed [M, K/2] uint8, x_scale [M, K/group] fp32)."""
+    q, s = quantize_groups(rotate(X, mode), inv_smooth, group)
+    return pack_int4(q), s
+
+
+def pack_weights_grouped(W, smooth=None, group: int = 128, mode: int = ROT_EXPLICIT):
+    """Grouped weight step: returns (Wq packed [N, K/2] uint8, w_scale [N, K/group] fp32)."""
+    q, s = quantize_groups(rotate(W, mode), smooth, group)
+    return pack_int4(q), s
+
+
+def dequant_grouped(qa, qw, sa, sw, bias=None, epi: int = 0) -> np.ndarray:
+    """Y = sum_g acc_g * sa[:, g] * sw[:, g] (+ bias) (+ GELU) in fp64 from int8 codes."""
+    qa = np.ascontiguousarray(np.asarray(qa, dtype=np.int8))
+    qw = np.ascontiguousarray(np.asarray(qw, dtype=np.int8))
+    M, K = qa.shape
+    N = qw.shape[0]
+    sa = np.ascontiguousarray(np.asarray(sa, dtype=np.float32))
+    sw = np.ascontiguousarray(np.asarray(sw, dtype=np.float32))
+    group = K // sa.shape[1]
+    Y = np.empty((M, N), dtype=np.float64)
+    bias = _f32(bias)
+    _check(lib().qvref_dequant_grouped(_p(qa), _p(qw), _p(sa), _p(sw), _p(bias), M, N, K, group, epi,
+                                       _p(Y)), "dequant_grouped")
+    return Y
+
+
+def w4a4_gemm_grouped(Xq, x_scale, Wq, w_scale, bias=None, epi: int = 0) -> np.ndarray:
+    """Grouped GEMM on packed codes: unpack, then dequant_grouped."""
+    return dequant_grouped(unpack_int4(Xq), unpack_int4(Wq), x_scale, w_scale, bias, epi)

@@ -296,3 +296,34 @@ int qvref_w4a4_linear(const double* X, int64_t M, int64_t K, int64_t ldx, const 
     free(xs);
     return rc;
 }
+
+/* Group-wise granularity ([P4] 双平滑细粒度量化（DSFQ） > 细粒度量化粒度, truncated on the page;
+ * reading: each row of activations and of weights carries one scale per group of `group`
+ * consecutive channels of the rotated, smoothed row, and the product sums the groups' integer dot
+ * products, each dequantized by its own pair of scales):
+ *   Y[m][n] = sum_g (sum_{k in g} qa[m][k] qw[n][k]) * sa[m][g] * sw[n][g] (+ bias[n]), in fp64,
+ *   then the erf GELU when epi = 1.  sa is [M][K/group], sw is [N][K/group], both row-major. */
+int qvref_dequant_grouped(const int8_t* qa, const int8_t* qw, const float* sa, const float* sw,
+                          const float* bias, int64_t M, int64_t N, int64_t K, int64_t group, int epi,
+                          double* Y) {
+    if (M < 0 || N < 0 || K <= 0 || group <= 0 || K % group != 0 || (epi != 0 && epi != 1)) return -1;
+    if (M == 0 || N == 0) return 0;
+    if (!qa || !qw || !sa || !sw || !Y) return -1;
+    const int64_t groups = K / group;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double y = 0.0;
+            for (int64_t g = 0; g < groups; ++g) {
+                int64_t acc = 0;
+                for (int64_t k = g * group; k < (g + 1) * group; ++k)
+                    acc += (int64_t)qa[m * K + k] * (int64_t)qw[n * K + k];
+                if (acc > INT32_MAX || acc < INT32_MIN) return -2;
+                y += (double)acc * (double)sa[m * groups + g] * (double)sw[n * groups + g];
+            }
+            if (bias) y += (double)bias[n];
+            if (epi == 1) y = qvref_gelu(y);
+            Y[m * N + n] = y;
+        }
+    }
+    return 0;
+}

@@ -77,6 +77,14 @@ int qvref_w4a4_linear(const double* X, int64_t M, int64_t K, int64_t ldx, const 
                       const uint8_t* Wq, const float* w_scale, const float* bias, int64_t N, int epi,
                       int rot_mode, double* Y);
 
+/* Group-wise granularity ([P4] 细粒度量化粒度; the subsection is truncated, see the reading in the
+ * implementation): Y[m][n] = sum_g (sum_{k in group g} qa[m][k] qw[n][k]) * sa[m][g] * sw[n][g]
+ * (+ bias[n]) in fp64, then the erf GELU when epi = 1.  qa [M][K], qw [N][K] int8 codes;
+ * sa [M][K/group], sw [N][K/group]; group divides K. */
+int qvref_dequant_grouped(const int8_t* qa, const int8_t* qw, const float* sa, const float* sw,
+                          const float* bias, int64_t M, int64_t N, int64_t K, int64_t group, int epi,
+                          double* Y);
+
 #ifdef __cplusplus
 }
 #endif

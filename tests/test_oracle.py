@@ -318,3 +318,89 @@ def test_rotation_and_smoothing_reduce_w4a4_error(oracle_mod):
     assert e_rot < e_none
     assert e_both < e_rot
     assert e_smooth < e_none
+
+
+# ------------------------------------------------ group-wise granularity ([P4] 细粒度量化粒度)
+
+def test_grouped_quantizer_with_one_group_is_the_row_quantizer(oracle_mod):
+    """A single group spanning the row is per-token quantization: codes and scales equal the
+    row quantizer's (pinned above), for activations and weights."""
+    X = synth.vggt_activations(9, 1024, seed=31)
+    inv = (0.5 + np.random.default_rng(3).random(1024)).astype(np.float32)
+    q1, s1 = O.quantize_groups(O.rotate(X), inv, group=1024)
+    q0, s0 = O.quantize_rows(O.rotate(X), inv)
+    np.testing.assert_array_equal(q1, q0)
+    np.testing.assert_array_equal(s1[:, 0], s0)
+
+
+@pytest.mark.parametrize("group", [128, 256, 512])
+def test_grouped_quantizer_constructed_ties_per_group(oracle_mod, group):
+    """Rotated targets t of half-integers with max |t| = 7 inside every group (x = t H / sqrt(d)
+    rotates back to t exactly) give scale 1 in every group and codes rint(t) (numpy's round half
+    to even, independent of the oracle)."""
+    d = 1024
+    rng = np.random.default_rng(group)
+    t = rng.integers(-13, 14, size=(4, d)).astype(np.float64) / 2.0
+    for g in range(d // group):
+        t[:, g * group] = 7.0 if g % 2 else -7.0
+    t[0, 1:7] = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5]
+    X = t @ O.hadamard(d).astype(np.float64) / np.sqrt(d)
+    Xq, s = O.hadamard_smooth_quant_grouped(X, None, group)
+    assert s.shape == (4, d // group) and np.all(s == np.float32(1.0))
+    np.testing.assert_array_equal(O.unpack_int4(Xq), np.rint(t).astype(np.int8))
+
+
+def test_grouped_quantizer_group_absmax_error_bound_and_zero_group(oracle_mod):
+    """Every group's absmax maps to +-7, every value lies within half a step of its group's grid,
+    and an all-zero group gets scale 0 and zero codes while its neighbours are quantized."""
+    group = 128
+    X = synth.vggt_activations(8, 1024, seed=32)
+    Xh = O.rotate(X)
+    Xh[3, 256:384] = 0.0
+    q, s = O.quantize_groups(Xh, None, group)
+    x32 = Xh.astype(np.float32).astype(np.float64)
+    for g in range(1024 // group):
+        sl = slice(g * group, (g + 1) * group)
+        err = np.abs(x32[:, sl] - q[:, sl] * s[:, g:g + 1].astype(np.float64))
+        assert np.all(err <= s[:, g:g + 1] * (0.5 + 1e-6))
+        live = s[:, g] > 0
+        assert np.all(np.abs(q[live, sl]).max(axis=1) == 7)
+    assert s[3, 2] == 0 and np.all(q[3, 256:384] == 0) and s[3, 1] > 0 and s[3, 3] > 0
+
+
+def test_grouped_dequant_equals_dequantize_then_matmul(oracle_mod):
+    """The grouped product equals, up to fp64 rounding, the matrix product of the dequantized
+    operands (each code times its group's scale), computed by numpy: a different evaluation order
+    of the same sum."""
+    rng = np.random.default_rng(33)
+    M, N, K, group = 7, 5, 512, 128
+    qa = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+    sa = rng.uniform(0.01, 2.0, size=(M, K // group)).astype(np.float32)
+    sw = rng.uniform(0.01, 2.0, size=(N, K // group)).astype(np.float32)
+    b = rng.standard_normal(N).astype(np.float32)
+    Xd = qa * np.repeat(sa.astype(np.float64), group, axis=1)
+    Wd = qw * np.repeat(sw.astype(np.float64), group, axis=1)
+    ref = Xd @ Wd.T + b.astype(np.float64)
+    np.testing.assert_allclose(O.dequant_grouped(qa, qw, sa, sw, b), ref, rtol=1e-12, atol=1e-12)
+    g = O.dequant_grouped(qa, qw, sa, sw, b, epi=1)
+    np.testing.assert_allclose(g, ref * scipy.special.ndtr(ref), rtol=1e-12, atol=1e-300)
+
+
+def test_grouped_dequant_special_cases(oracle_mod):
+    """Unit scales give the integer product over the whole row (the pinned int GEMM); scales equal
+    across groups give the per-token dequantization; a single nonzero group contributes alone."""
+    rng = np.random.default_rng(34)
+    M, N, K, group = 6, 4, 1024, 256
+    qa = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+    ones_a, ones_w = np.ones((M, K // group), np.float32), np.ones((N, K // group), np.float32)
+    np.testing.assert_array_equal(O.dequant_grouped(qa, qw, ones_a, ones_w), O.gemm_int(qa, qw).astype(np.float64))
+    a = rng.uniform(0.1, 1, M).astype(np.float32)
+    w = rng.uniform(0.1, 1, N).astype(np.float32)
+    got = O.dequant_grouped(qa, qw, np.repeat(a[:, None], K // group, 1), np.repeat(w[:, None], K // group, 1))
+    np.testing.assert_allclose(got, O.dequant(O.gemm_int(qa, qw), a, w), rtol=1e-14)
+    qa1 = np.zeros_like(qa)
+    qa1[:, 512:768] = qa[:, 512:768]
+    got = O.dequant_grouped(qa1, qw, ones_a * 3.0, ones_w * 0.5)
+    np.testing.assert_array_equal(got, 1.5 * (qa[:, 512:768].astype(np.int64) @ qw[:, 512:768].T.astype(np.int64)))
