@@ -316,11 +316,11 @@ int qvref_dequant_grouped(const int8_t* qa, const int8_t* qw, const float* sa, c
             for (int64_t g = 0; g < groups; ++g) {
                 int64_t acc = 0;
                 for (int64_t k = g * group; k < (g + 1) * group; ++k)
-                    acc += (int64_t)qa[m * K + k] * (int64_t)qw[n * K + k];
+                    acc += (int64_t)qa[m * K + k] * qw[n * K + k];
                 if (acc > INT32_MAX || acc < INT32_MIN) return -2;
                 y += (double)acc * (double)sa[m * groups + g] * (double)sw[n * groups + g];
             }
-            if (bias) y += (double)bias[n];
+            if (bias != NULL) y += (double)bias[n];
             if (epi == 1) y = qvref_gelu(y);
             Y[m * N + n] = y;
         }

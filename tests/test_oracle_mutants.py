@@ -26,6 +26,11 @@ MUTANTS = {
     "gemm_transposed_weight": ("(int64_t)qw[n * K + k];", "(int64_t)qw[k * N + n];"),
     "dequant_drops_bias": ("if (bias) y += (double)bias[n];", ""),
     "gelu_wrong_sign": ("return 0.5 * y * erfc(-y / sqrt(2.0));", "return 0.5 * y * erfc(y / sqrt(2.0));"),
+    "grouped_scale_ignores_group": ("y += (double)acc * (double)sa[m * groups + g] * (double)sw[n * groups + g];",
+                                    "y += (double)acc * (double)sa[m * groups + g] * (double)sw[n * groups];"),
+    "grouped_drops_last_channel": ("for (int64_t k = g * group; k < (g + 1) * group; ++k)",
+                                   "for (int64_t k = g * group; k < (g + 1) * group - 1; ++k)"),
+    "grouped_drops_bias": ("if (bias != NULL) y += (double)bias[n];", ""),
     "smoothing_alpha_swapped": ("sk = pow(ax, alpha) / pow(aw, 1.0 - alpha);", "sk = pow(ax, 1.0 - alpha) / pow(aw, alpha);"),
 }
 
