@@ -36,6 +36,8 @@ def parse_args():
                    help="untimed steps first: the GPU clock needs tens of milliseconds of load to ramp up from idle")
     p.add_argument("--workload", default="block_32frames")
     p.add_argument("--no-w8a8", dest="w8a8", action="store_false", help="skip the W8A8 line")
+    p.add_argument("--group", type=int, default=128,
+                   help="group size of the group-wise line (128, 256 or 512; 0 to skip it)")
     p.add_argument("--secondary", default="qkv_8frames",
                    help="a second workload timed the same way after the main one ('' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
@@ -318,6 +320,38 @@ def main():
                           "gemm_TOPS": round(k2_ops / g8 / 1e12, 2), "gemm_frac": round(k2_ops / g8 / 1e12 / PEAK_INT8_TOPS, 4),
                           "rotate_quant_GBps": round(b8 / q8 / 1e9, 1)}
         del layers8
+
+    # ---------------------------------------------------------------- group-wise scales, same workload
+    if args.group:
+        torch.cuda.empty_cache()
+        G = args.group
+        layersg = workload.build(qv, wl, dev, share_outputs=wl.blocks > 1, group=G)
+
+        def stepg():
+            for L in layersg:
+                workload.run_linear(qv, L, stream)
+
+        for _ in range(args.warmup):
+            stepg()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            stepg()
+        torch.cuda.synchronize()
+        wg = (time.perf_counter() - t0) / args.steps
+        gg = timed(lambda: [qv.qv_w4a4_gemm_grouped(L.Xq, L.xs, L.Wq, L.ws, None, L.Y, G, L.lin.epi, stream)
+                            for _ in range(reps) for L in layersg]) / (reps * len(layersg))
+        qg = timed(lambda: [qv.qv_hadamard_smooth_quant_grouped(L.X, L.inv, G, L.Xq, L.xs, stream)
+                            for _ in range(reps) for L in layersg]) / (reps * len(layersg))
+        bg = sum(M * L.lin.K * L.X.element_size() + M * (L.lin.K // 2) + 4 * M * (L.lin.K // G)
+                 for L in layersg) / len(layersg)
+        result["grouped"] = {"what": f"the same workload with one scale per row and group of {G} channels "
+                                     "(group-wise dequantization in the GEMM's K loop)",
+                             "group": G, "value": round(ops_per_step / wg / 1e12, 2), "unit": "TOPS",
+                             "ms_per_step": round(1e3 * wg, 4), "gemm_TOPS": round(k2_ops / gg / 1e12, 2),
+                             "gemm_frac": round(k2_ops / gg / 1e12 / PEAK_INT8_TOPS, 4),
+                             "rotate_quant_GBps": round(bg / qg / 1e9, 1)}
+        del layersg
 
     print(json.dumps(result))
 

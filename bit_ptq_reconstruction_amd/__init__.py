@@ -63,9 +63,17 @@ def lib():
         L.qv_w8a8_linear_workspace_size.argtypes = [i64, i64]
         L.qv_w8a8_linear_workspace_size.restype = sz
         L.qv_w8a8_linear.argtypes = [P, i32, i64, i64, i64, P, P, P, P, i64, i32, P, i32, i64, P, sz, P]
+        L.qv_hadamard_smooth_quant_grouped.argtypes = [P, i32, i64, i64, i64, P, i64, P, P, P]
+        L.qv_pack_weights_grouped.argtypes = [P, i32, i64, i64, i64, P, i64, P, P, P]
+        L.qv_w4a4_gemm_grouped.argtypes = [P, P, P, P, P, i64, i64, i64, i64, i32, P, i32, i64, P]
+        L.qv_w4a4_linear_grouped_workspace_size.argtypes = [i64, i64, i64]
+        L.qv_w4a4_linear_grouped_workspace_size.restype = sz
+        L.qv_w4a4_linear_grouped.argtypes = [P, i32, i64, i64, i64, P, i64, P, P, P, i64, i32, P, i32, i64, P, sz,
+                                             P]
         for name in ("qv_hadamard_smooth_quant", "qv_pack_weights", "qv_w4a4_gemm", "qv_w4a4_linear",
                      "qv_smooth_calibrate", "qv_hadamard_smooth_quant8", "qv_pack_weights8", "qv_w8a8_gemm",
-                     "qv_w8a8_linear"):
+                     "qv_w8a8_linear", "qv_hadamard_smooth_quant_grouped", "qv_pack_weights_grouped",
+                     "qv_w4a4_gemm_grouped", "qv_w4a4_linear_grouped"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -189,3 +197,55 @@ def qv_w8a8_linear(X, inv_smooth, Wq8, w_scale, bias, Y, workspace, epi: int = Q
     _check(lib().qv_w8a8_linear(_ptr(X), _dtype(X), M, K, _ld(X), _ptr(inv_smooth), _ptr(Wq8), _ptr(w_scale),
                                 _ptr(bias), N, int(epi), _ptr(Y), _dtype(Y), _ld(Y), _ptr(workspace), nbytes,
                                 _stream(stream)), "qv_w8a8_linear")
+
+
+# -------------------------------------------------------------------------- group-wise granularity
+
+def _group_scales(scale, rows: int, K: int, group: int) -> None:
+    if tuple(scale.shape) != (rows, K // group) or not scale.is_contiguous():
+        raise ValueError(f"group scales must be a contiguous [{rows}, {K // group}] tensor")
+
+
+def qv_hadamard_smooth_quant_grouped(X, inv_smooth, group: int, Xq, x_scale, stream=None) -> None:
+    """X [M, K] fp32/bf16 -> Xq [M, K/2] uint8 (packed int4), x_scale [M, K/group] fp32."""
+    M, K = X.shape
+    _group_scales(x_scale, M, K, group)
+    _check(lib().qv_hadamard_smooth_quant_grouped(_ptr(X), _dtype(X), M, K, _ld(X), _ptr(inv_smooth), int(group),
+                                                  _ptr(Xq), _ptr(x_scale), _stream(stream)),
+           "qv_hadamard_smooth_quant_grouped")
+
+
+def qv_pack_weights_grouped(W, smooth, group: int, Wq, w_scale, stream=None) -> None:
+    """W [N, K] fp32/bf16 -> Wq [N, K/2] uint8 (packed int4), w_scale [N, K/group] fp32."""
+    N, K = W.shape
+    _group_scales(w_scale, N, K, group)
+    _check(lib().qv_pack_weights_grouped(_ptr(W), _dtype(W), N, K, _ld(W), _ptr(smooth), int(group), _ptr(Wq),
+                                         _ptr(w_scale), _stream(stream)), "qv_pack_weights_grouped")
+
+
+def qv_w4a4_gemm_grouped(Xq, x_scale, Wq, w_scale, bias, Y, group: int, epi: int = QV_EPI_NONE, stream=None) -> None:
+    """Y [M, N] = sum over groups of dequantized int4 dot products (+ bias) (+ GELU)."""
+    M, Kh = Xq.shape
+    N = Wq.shape[0]
+    _group_scales(x_scale, M, 2 * Kh, group)
+    _group_scales(w_scale, N, 2 * Kh, group)
+    _check(lib().qv_w4a4_gemm_grouped(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), _ptr(bias), M, N, 2 * Kh,
+                                      int(group), int(epi), _ptr(Y), _dtype(Y), _ld(Y), _stream(stream)),
+           "qv_w4a4_gemm_grouped")
+
+
+def qv_w4a4_linear_grouped_workspace_size(M: int, K: int, group: int) -> int:
+    return int(lib().qv_w4a4_linear_grouped_workspace_size(int(M), int(K), int(group)))
+
+
+def qv_w4a4_linear_grouped(X, inv_smooth, group: int, Wq, w_scale, bias, Y, workspace, epi: int = QV_EPI_NONE,
+                           stream=None) -> None:
+    """The whole online layer with group-wise scales; ``workspace`` holds at least
+    ``qv_w4a4_linear_grouped_workspace_size(M, K, group)`` bytes."""
+    M, K = X.shape
+    N = Wq.shape[0]
+    _group_scales(w_scale, N, K, group)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().qv_w4a4_linear_grouped(_ptr(X), _dtype(X), M, K, _ld(X), _ptr(inv_smooth), int(group), _ptr(Wq),
+                                        _ptr(w_scale), _ptr(bias), N, int(epi), _ptr(Y), _dtype(Y), _ld(Y),
+                                        _ptr(workspace), nbytes, _stream(stream)), "qv_w4a4_linear_grouped")

@@ -50,6 +50,14 @@ qv_status check_gemm(const void* Xq, const float* xs, const void* Wq, const floa
 
 size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
+// Group sizes of the group-wise variant: 128, 256 or 512 channels, dividing K, at most
+// qv::kMaxGroups groups per row.
+qv_status check_group(int64_t K, int64_t group) {
+  if (group != 128 && group != 256 && group != 512) return QV_ERR_UNSUPPORTED;
+  if (K <= 0 || (K % group) != 0 || K / group > qv::kMaxGroups) return QV_ERR_UNSUPPORTED;
+  return QV_OK;
+}
+
 qv_status hip_status(hipError_t e) { return e == hipSuccess ? QV_OK : QV_ERR_HIP; }
 
 }  // namespace
@@ -230,6 +238,85 @@ qv_status qv_w8a8_linear(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, 
     if (st != QV_OK) return st;
     return hip_status(
         qv::launch_w8a8_gemm(xq, xs, Wq8, w_scale, bias, M, N, K, epi == QV_EPI_GELU, Y, y_dtype == QV_BF16, ldy, s));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
+// ------------------------------------------------------------------ group-wise granularity
+
+qv_status qv_hadamard_smooth_quant_grouped(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                           const float* inv_smooth, int64_t group, uint8_t* Xq, float* x_scale,
+                                           void* hip_stream) {
+  try {
+    qv_status st = check_rotate_quant(X, x_dtype, M, K, ldx, inv_smooth, Xq, x_scale);
+    if (st == QV_OK) st = check_group(K, group);
+    if (st != QV_OK || M == 0) return st;
+    return hip_status(qv::launch_rotate_quant_grouped(X, x_dtype == QV_BF16, M, K, ldx, inv_smooth, group, Xq,
+                                                      x_scale, static_cast<hipStream_t>(hip_stream)));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
+qv_status qv_pack_weights_grouped(const void* W, qv_dtype w_dtype, int64_t N, int64_t K, int64_t ldw,
+                                  const float* smooth, int64_t group, uint8_t* Wq, float* w_scale,
+                                  void* hip_stream) {
+  try {
+    qv_status st = check_rotate_quant(W, w_dtype, N, K, ldw, smooth, Wq, w_scale);
+    if (st == QV_OK) st = check_group(K, group);
+    if (st != QV_OK || N == 0) return st;
+    return hip_status(qv::launch_rotate_quant_grouped(W, w_dtype == QV_BF16, N, K, ldw, smooth, group, Wq, w_scale,
+                                                      static_cast<hipStream_t>(hip_stream)));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
+qv_status qv_w4a4_gemm_grouped(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq, const float* w_scale,
+                               const float* bias, int64_t M, int64_t N, int64_t K, int64_t group, qv_epilogue epi,
+                               void* Y, qv_dtype y_dtype, int64_t ldy, void* hip_stream) {
+  try {
+    qv_status st = check_gemm(Xq, x_scale, Wq, w_scale, bias, M, N, K, epi, Y, y_dtype, ldy);
+    if (st == QV_OK) st = check_group(K, group);
+    if (st != QV_OK || M == 0 || N == 0) return st;
+    return hip_status(qv::launch_w4a4_gemm_grouped(Xq, x_scale, Wq, w_scale, bias, M, N, K, group,
+                                                   epi == QV_EPI_GELU, Y, y_dtype == QV_BF16, ldy,
+                                                   static_cast<hipStream_t>(hip_stream)));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
+size_t qv_w4a4_linear_grouped_workspace_size(int64_t M, int64_t K, int64_t group) {
+  if (M < 0 || check_group(K, group) != QV_OK) return 0;
+  return round256(static_cast<size_t>(M) * static_cast<size_t>(K / 2)) +
+         round256(static_cast<size_t>(M) * static_cast<size_t>(K / group) * 4);
+}
+
+qv_status qv_w4a4_linear_grouped(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                 const float* inv_smooth, int64_t group, const uint8_t* Wq, const float* w_scale,
+                                 const float* bias, int64_t N, qv_epilogue epi, void* Y, qv_dtype y_dtype,
+                                 int64_t ldy, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  try {
+    qv_status st = check_rotate_quant(X, x_dtype, M, K, ldx, inv_smooth, reinterpret_cast<uint8_t*>(16),
+                                      reinterpret_cast<float*>(16));
+    if (st == QV_OK) st = check_group(K, group);
+    if (st != QV_OK) return st;
+    st = check_gemm(reinterpret_cast<uint8_t*>(16), reinterpret_cast<float*>(16), Wq, w_scale, bias, M, N, K, epi,
+                    Y, y_dtype, ldy);
+    if (st != QV_OK) return st;
+    if (M == 0 || N == 0) return QV_OK;
+    const size_t need = qv_w4a4_linear_grouped_workspace_size(M, K, group);
+    if (!workspace || workspace_bytes < need) return QV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) % 256) != 0) return QV_ERR_ALIGN;
+    uint8_t* xq = static_cast<uint8_t*>(workspace);
+    float* xs = reinterpret_cast<float*>(xq + round256(static_cast<size_t>(M) * static_cast<size_t>(K / 2)));
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    st = hip_status(qv::launch_rotate_quant_grouped(X, x_dtype == QV_BF16, M, K, ldx, inv_smooth, group, xq, xs, s));
+    if (st != QV_OK) return st;
+    return hip_status(qv::launch_w4a4_gemm_grouped(xq, xs, Wq, w_scale, bias, M, N, K, group, epi == QV_EPI_GELU, Y,
+                                                   y_dtype == QV_BF16, ldy, s));
   } catch (...) {
     return QV_ERR_INTERNAL;
   }

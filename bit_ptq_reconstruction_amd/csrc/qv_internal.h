@@ -18,6 +18,19 @@ hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* xs, const uint8_t* W
                             const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out,
                             int64_t ldy, hipStream_t st);
 
+// Group-wise variant of the rotate-quantize step: one scale per row and group of `group` in
+// {128, 256, 512} channels, scale[row][K / group].
+hipError_t launch_rotate_quant_grouped(const void* X, bool bf16, int64_t M, int64_t K, int64_t ld, const float* mult,
+                                       int64_t group, uint8_t* q, float* scale, hipStream_t st);
+
+// Int4 x int4 GEMM with group-wise scales (xs [M][K / group], ws [N][K / group], group in
+// {128, 256, 512}, K / group <= kMaxGroups): each group's integer dot products dequantized by its
+// own pair of scales and summed in fp32, then the same epilogue.
+constexpr int kMaxGroups = 32;
+hipError_t launch_w4a4_gemm_grouped(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws,
+                                    const float* bias, int64_t M, int64_t N, int64_t K, int64_t group, bool gelu,
+                                    void* Y, bool bf16_out, int64_t ldy, hipStream_t st);
+
 // Int8 x int8 GEMM (N % 128 == 0, K % 64 == 0) with the same epilogue.
 hipError_t launch_w8a8_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
                             const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out,

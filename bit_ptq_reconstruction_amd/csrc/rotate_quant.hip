@@ -130,11 +130,35 @@ __device__ __forceinline__ void fill_multiplier_table(const float* __restrict__ 
   }
 }
 
-template <int K, typename In, int kBits>
+// Maximum over the 16 lanes of a DPP row.
+__device__ __forceinline__ float lanes16_max(float x) {
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, true)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, true)));
+  return x;
+}
+
+// Group-wise scales (kGroup = 128, 256 or 512 channels; 0 = one scale per row).  After the
+// transform register group j of a lane holds 8 consecutive channels 8 dword_index(lane, j) + 0..7,
+// and the 16 lanes of a DPP row hold the 16 chunks of one aligned 128-channel block, so a
+// 128-channel group is one j across a DPP row; 256 channels pair j with j ^ 1 and 512 channels
+// join j, j ^ 1, j ^ 2 (dword_index(lane, j) / 16 steps by one with j bit 0 and by two with j bit 1,
+// for both widths).  A group's maximum is therefore an in-lane max over those j and a max over the
+// DPP row, and its index is 8 dword_index / kGroup.
+template <int K, int kGroup>
+__device__ __forceinline__ int group_of(int lane, int j) {
+  return 8 * dword_index<K>(lane & ~15, j) / kGroup;
+}
+
+template <int K, typename In, int kBits, int kGroup>
 __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const In* __restrict__ X, int64_t M, int64_t ldx,
                                                                const float* __restrict__ mult,
                                                                uint8_t* __restrict__ Xq,
                                                                float* __restrict__ x_scale) {
+  static_assert(kGroup == 0 || kGroup == 128 || kGroup == 256 || kGroup == 512, "group size");
+  static_assert(kGroup == 0 || kBits == 4, "group-wise scales are built for 4-bit codes");
+  constexpr int kJoin = kGroup == 512 ? 3 : (kGroup == 256 ? 1 : 0);  // j bits joined in a group
   using L = RowLayout<K>;
   __shared__ __attribute__((aligned(16))) float cm_lds[(K == 1024 ? 16 : 64) * kCmStride];
   const int lane = threadIdx.x & 63;
@@ -173,29 +197,58 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const In* __rest
 
     fwht_row_regs<K>(v, lane);
 
-    float amax = 0.0f;
+    float gmax[8];  // per register group j: the maximum of |smoothed value| over its channels
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float4 c0 = *reinterpret_cast<const float4*>(cm_row + 8 * j);
       const float4 c1 = *reinterpret_cast<const float4*>(cm_row + 8 * j + 4);
       const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      gmax[j] = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         v[j][e] *= c[e];
-        amax = fmaxf(amax, fabsf(v[j][e]));
+        gmax[j] = fmaxf(gmax[j], fabsf(v[j][e]));
       }
     }
-    amax = row_max<K>(amax);
-    float s = amax / (float)((1 << (kBits - 1)) - 1);
-    if (!(s >= 1.17549435e-38f)) s = 0.0f;  // zero or subnormal scale: all-zero row
-    const float r = (s > 0.0f) ? 1.0f / s : 0.0f;
+    // Scale and reciprocal of each register group's quantization group (the whole row, or one
+    // group of channels).
+    float sg[8], rg[8];
+    constexpr float kQmax = (float)((1 << (kBits - 1)) - 1);
+    if constexpr (kGroup == 0) {
+      float amax = gmax[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) amax = fmaxf(amax, gmax[j]);
+      amax = row_max<K>(amax);
+      float s = amax / kQmax;
+      if (!(s >= 1.17549435e-38f)) s = 0.0f;  // zero or subnormal scale: all-zero row
+      const float r = (s > 0.0f) ? 1.0f / s : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { sg[j] = s; rg[j] = r; }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if ((j & kJoin) == 0) {  // the group's first register group computes, the others copy
+          float a = gmax[j];
+          if constexpr (kJoin & 1) a = fmaxf(a, gmax[j | 1]);
+          if constexpr (kJoin & 2) a = fmaxf(fmaxf(a, gmax[j | 2]), gmax[j | 3]);
+          a = lanes16_max(a);
+          float s = a / kQmax;
+          if (!(s >= 1.17549435e-38f)) s = 0.0f;  // zero or subnormal scale: all-zero group
+          sg[j] = s;
+          rg[j] = (s > 0.0f) ? 1.0f / s : 0.0f;
+        } else {
+          sg[j] = sg[j & ~kJoin];
+          rg[j] = rg[j & ~kJoin];
+        }
+      }
+    }
 
     if (row < M) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         uint32_t m[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m[e] = __builtin_bit_cast(uint32_t, __builtin_fmaf(v[j][e], r, kMagic<kBits>));
+        for (int e = 0; e < 8; ++e) m[e] = __builtin_bit_cast(uint32_t, __builtin_fmaf(v[j][e], rg[j], kMagic<kBits>));
         // the lane's eight codes of group j are k = 8 dword_index + 0..7
         if constexpr (kBits == 4) {
           reinterpret_cast<uint32_t*>(Xq + row * (K / 2))[dword_index<K>(lane, j)] = pack8(m);
@@ -203,7 +256,17 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const In* __rest
           reinterpret_cast<uint2*>(Xq + row * K)[dword_index<K>(lane, j)] = pack8_int8(m);
         }
       }
-      if ((lane & (L::kLanesPerRow - 1)) == 0) x_scale[row] = s;
+      if constexpr (kGroup == 0) {
+        if ((lane & (L::kLanesPerRow - 1)) == 0) x_scale[row] = sg[0];
+      } else {
+        // the first lane of each DPP row writes the scales of the groups its row holds
+        constexpr int kGroups = K / kGroup;
+        if ((lane & 15) == 0) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if ((j & kJoin) == 0) x_scale[row * kGroups + group_of<K, kGroup>(lane, j)] = sg[j];
+        }
+      }
     }
   }
 }
@@ -289,13 +352,21 @@ int grid_for_rows(int64_t M, int rows_per_wave, int resident) {
   return (int)(blocks < resident ? blocks : resident);
 }
 
-template <int K, typename In, int kBits>
+template <int K, typename In, int kBits, int kGroup = 0>
 hipError_t launch_rq(const void* X, int64_t M, int64_t ld, const float* mult, uint8_t* q, float* scale,
                      hipStream_t st) {
-  const int grid = grid_for_rows(M, RowLayout<K>::kRowsPerWave, resident_grid<rotate_quant_kernel<K, In, kBits>>());
-  hipLaunchKernelGGL((rotate_quant_kernel<K, In, kBits>), dim3(grid), dim3(kThreads), 0, st,
+  const int grid =
+      grid_for_rows(M, RowLayout<K>::kRowsPerWave, resident_grid<rotate_quant_kernel<K, In, kBits, kGroup>>());
+  hipLaunchKernelGGL((rotate_quant_kernel<K, In, kBits, kGroup>), dim3(grid), dim3(kThreads), 0, st,
                      static_cast<const In*>(X), M, ld, mult, q, scale);
   return hipGetLastError();
+}
+
+template <int K, int kGroup>
+hipError_t launch_rq_grouped(const void* X, bool bf16, int64_t M, int64_t ld, const float* mult, uint8_t* q,
+                             float* scale, hipStream_t st) {
+  return bf16 ? launch_rq<K, uint16_t, 4, kGroup>(X, M, ld, mult, q, scale, st)
+              : launch_rq<K, float, 4, kGroup>(X, M, ld, mult, q, scale, st);
 }
 
 template <int K, typename In>
@@ -324,6 +395,18 @@ hipError_t launch_rotate_quant(const void* X, bool bf16, int64_t M, int64_t K, i
   }
   return bf16 ? launch_rq<4096, uint16_t, 4>(X, M, ld, mult, q, scale, st)
               : launch_rq<4096, float, 4>(X, M, ld, mult, q, scale, st);
+}
+
+hipError_t launch_rotate_quant_grouped(const void* X, bool bf16, int64_t M, int64_t K, int64_t ld, const float* mult,
+                                       int64_t group, uint8_t* q, float* scale, hipStream_t st) {
+  if (K == 1024) {
+    if (group == 128) return launch_rq_grouped<1024, 128>(X, bf16, M, ld, mult, q, scale, st);
+    if (group == 256) return launch_rq_grouped<1024, 256>(X, bf16, M, ld, mult, q, scale, st);
+    return launch_rq_grouped<1024, 512>(X, bf16, M, ld, mult, q, scale, st);
+  }
+  if (group == 128) return launch_rq_grouped<4096, 128>(X, bf16, M, ld, mult, q, scale, st);
+  if (group == 256) return launch_rq_grouped<4096, 256>(X, bf16, M, ld, mult, q, scale, st);
+  return launch_rq_grouped<4096, 512>(X, bf16, M, ld, mult, q, scale, st);
 }
 
 hipError_t launch_smooth_calibrate(const void* Xc, bool xbf16, int64_t Mc, int64_t ldx, const void* W, bool wbf16,

@@ -147,16 +147,22 @@ struct GemmLds {
 // 64 x 64 wave tiles with a 2-deep ring of 64-byte stages fit four 4-wave or two 8-wave blocks per
 // CU; a 3-deep ring leaves room for three 4-wave blocks; the 128-accumulator wave tiles and the
 // 128-byte stages allow two.
-template <int BN, int BM, int WGN, int WGM, int RB, int STAGES>
+template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, int kGS = 0>
 constexpr int waves_per_eu() {
+  if (kGS > 0) return 2;  // group-wise scales: an fp32 accumulator beside the int32 one
   return (RB == 128 || (BN / WGN) * (BM / WGM) > 4096) ? 2 : ((WGN * WGM == 8 || STAGES == 2) ? 4 : 3);
 }
 
+typedef float v16f __attribute__((ext_vector_type(16)));
+
 // kW8: int8 operands (one code per byte, no widening, the accumulator is acc itself) instead of
-// packed int4.
-template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias, bool kW8>
+// packed int4.  kGS > 0: group-wise scales, one per row and group of 128 kGS channels (kGS stages
+// of 128 codes): x_scale is [M][K / (128 kGS)], w_scale [N][K / (128 kGS)], and each group's int32
+// accumulator is dequantized into an fp32 accumulator when the group's last stage is done.
+template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias, bool kW8,
+          int kGS = 0>
 __global__ __launch_bounds__(64 * WGN * WGM)
-__attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES>()))) void w4a4_gemm_kernel(const uint8_t* __restrict__ Xq,
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kGS>()))) void w4a4_gemm_kernel(const uint8_t* __restrict__ Xq,
                                                             const float* __restrict__ x_scale,
                                                             const uint8_t* __restrict__ Wq,
                                                             const float* __restrict__ w_scale,
@@ -175,6 +181,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES>())
   constexpr int kStageBytes = (BN + BM) * kRowBytes;
   static_assert(kUnits % kThr == 0, "tile must split evenly over the waves");
   static_assert(STAGES >= 2 && (STAGES - 2) * kLoads < 64, "pipeline depth");
+  static_assert(kGS == 0 || (!kW8 && RB == 64), "group-wise scales: int4 operands, 128-code stages");
   static_assert((BN + BM) % 64 == 0, "whole waves of scale loads");
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
@@ -252,22 +259,27 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES>())
   // The tile's scales: scale slot i holds w_scale[n0 + i] (i < BN) or x_scale[m0 + i - BN] (rows
   // past M repeat the last row); thread t fetches slots t, t + kThr, ...  Issued before the stage
   // loads, so the first iteration's vmcnt wait covers them.
+  // Group-wise scales: the same for every group g, into slots g (BN + BM) + i, from column g of the
+  // [rows][groups] scale matrices.
   float* const scales = reinterpret_cast<float*>(lds + GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out>::kScaleOffset);
+  const int groups = kGS > 0 ? (int)(K / (128 * kGS)) : 1;  // groups of 128 kGS channels
+  for (int g = 0; g < groups; ++g) {
 #pragma unroll
-  for (int r = 0; r < (BN + BM + kThr - 1) / kThr; ++r) {
-    const int i = tid + kThr * r;
-    if (kThr * r + 64 * wave >= BN + BM) break;  // wave-uniform
-    const float* sp;
-    if (i < BN) {
-      sp = w_scale + n0 + i;
-    } else {
-      const int64_t mr = m0 + (i - BN);
-      sp = x_scale + (mr < M ? mr : M - 1);
+    for (int r = 0; r < (BN + BM + kThr - 1) / kThr; ++r) {
+      const int i = tid + kThr * r;
+      if (kThr * r + 64 * wave >= BN + BM) break;  // wave-uniform
+      const float* sp;
+      if (i < BN) {
+        sp = w_scale + (n0 + i) * groups + g;
+      } else {
+        const int64_t mr = m0 + (i - BN);
+        sp = x_scale + (mr < M ? mr : M - 1) * groups + g;
+      }
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(sp),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                           reinterpret_cast<uintptr_t>(scales + g * (BN + BM) + 64 * (wave + kWaves * r))),
+                                       4, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(sp),
-                                     reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                         reinterpret_cast<uintptr_t>(scales + 64 * (wave + kWaves * r))),
-                                     4, 0, 0);
   }
   if constexpr (QV_DMA) {
 #pragma unroll
@@ -282,7 +294,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES>())
       }
   }
 
-  for (int kt = 0; kt < nk; ++kt) {
+  // One stage: wait for stage kt, refill the ring, read and widen the fragments, 16 MFMAs.  A
+  // "fresh" stage starts its accumulators from zero (the first stage of a group of channels).
+  auto stage_step = [&](int kt, auto fresh) {
+    constexpr bool kFresh = decltype(fresh)::value;
     if constexpr (QV_DMA) {
       // Stage kt has landed once at most STAGES - 2 later stages are still in flight.
       if (kt + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * kLoads>();
@@ -339,7 +354,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES>())
           const uint32_t p0 = pb[c][s >> 1][2 * (s & 1)], p1 = pb[c][s >> 1][2 * (s & 1) + 1];
           const v4i fb = widen(p0, p1);
 #pragma unroll
-          for (int a = 0; a < FN; ++a) acc[a][c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[a], fb, acc[a][c], 0, 0, 0);
+          for (int a = 0; a < FN; ++a) acc[a][c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[a], fb, (kFresh && s == 0) ? v16i{} : acc[a][c], 0, 0, 0);
         }
       }
       // Schedule: the fragment reads, the first sub-step's widening, then one MFMA per three VALU
@@ -357,6 +372,42 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES>())
       // The buffer of stage kt + STAGES - 1 held stage kt - 1, which every wave finished reading
       // before this iteration's barrier.
       if (refill) store_stage((kt + STAGES - 1) % STAGES);
+    }
+  };
+
+  v16f facc[kGS > 0 ? FN : 1][kGS > 0 ? FM : 1];
+  if constexpr (kGS > 0) {
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+      for (int c = 0; c < FM; ++c) facc[a][c] = v16f{};
+  }
+  (void)facc;
+  if constexpr (kGS == 0) {
+    for (int kt = 0; kt < nk; ++kt) stage_step(kt, std::false_type{});
+  } else {
+    // Groups of kGS stages; after each, acc (256 x the group's integer dot products) is
+    // dequantized with the group's scales into facc: the row scale carries the 2^-8.
+    for (int kt0 = 0; kt0 < nk; kt0 += kGS) {
+      stage_step(kt0, std::true_type{});
+#pragma unroll
+      for (int st = 1; st < kGS; ++st) stage_step(kt0 + st, std::false_type{});
+      const float* sg = scales + (kt0 / kGS) * (BN + BM);
+#pragma unroll
+      for (int c = 0; c < FM; ++c) {
+        const float sa = sg[BN + wm * WM + 32 * c + r32] * 0.00390625f;
+#pragma unroll
+        for (int a = 0; a < FN; ++a) {
+#pragma unroll
+          for (int vg = 0; vg < 4; ++vg) {
+            const float4 sw4 = *reinterpret_cast<const float4*>(sg + wn * WN + 32 * a + 8 * vg + 4 * h);
+            const float sw[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              facc[a][c][4 * vg + v] = __builtin_fmaf((float)acc[a][c][4 * vg + v] * sa, sw[v], facc[a][c][4 * vg + v]);
+          }
+        }
+      }
     }
   }
 
@@ -385,7 +436,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES>())
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      y[v] = (float)acc[a][c][4 * vg + v] * sa[c] * sw[v];
+      if constexpr (kGS > 0) {
+        y[v] = facc[a][c][4 * vg + v];
+      } else {
+        y[v] = (float)acc[a][c][4 * vg + v] * sa[c] * sw[v];
+      }
       if constexpr (kBias) y[v] += bb[v];
       if constexpr (kGelu) y[v] = gelu(y[v]);
     }
@@ -478,28 +533,32 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES>())
   }
 }
 
-template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias, bool kW8>
+template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias, bool kW8,
+          int kGS = 0>
 hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
                     int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
-  constexpr size_t kLds = GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out>::kTotal;
+  using Lds = GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out>;
+  // Group-wise scales take one (BN + BM)-float slot per group, at most kMaxGroups of them.
+  const size_t lds = kGS > 0 ? Lds::kScaleOffset + 4 * (size_t)(BN + BM) * (size_t)(K / (128 * kGS)) : Lds::kTotal;
+  constexpr size_t kLdsMax = kGS > 0 ? Lds::kScaleOffset + 4 * (size_t)(BN + BM) * kMaxGroups : Lds::kTotal;
   static int attr_set[16] = {0};  // per device: allow more than 64 KB of dynamic LDS once
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
   if (!attr_set[dev]) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias, kW8>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+        reinterpret_cast<const void*>(&w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias, kW8, kGS>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
     if (e != hipSuccess) return e;
     attr_set[dev] = 1;
   }
   const int64_t blocks = (N / BN) * ((M + BM - 1) / BM);
-  hipLaunchKernelGGL((w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias, kW8>), dim3((unsigned)blocks),
-                     dim3(64 * WGN * WGM), kLds, st, Xq, xs, Wq, ws, bias, M, N, K, Y, ldy);
+  hipLaunchKernelGGL((w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias, kW8, kGS>),
+                     dim3((unsigned)blocks), dim3(64 * WGN * WGM), lds, st, Xq, xs, Wq, ws, bias, M, N, K, Y, ldy);
   return hipGetLastError();
 }
 
 // Tile configurations (block tile BN x BM, wave grid WGN x WGM):
-//   0: 128 x 128, 2 x 2 waves of 64 x 64: 134 registers and 49 KB of LDS, three blocks per CU, so
+//   0: 128 x 128, 2 x 2 waves of 64 x 64: 128 registers and 36 KB of LDS, four blocks per CU, so
 //      one block's barrier, prologue and epilogue overlap the others' MFMAs;
 //   1: 256 x 256, 2 x 4 waves of 128 x 64; 2: 256 x 256, 4 x 2 waves of 64 x 128 (one block per
 //      CU, half the LDS-DMA bytes per MFMA);
@@ -568,6 +627,33 @@ hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* xs, const uint8_t* W
                             const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out,
                             int64_t ldy, hipStream_t st) {
   return launch_gemm<false>(Xq, xs, Wq, ws, bias, M, N, K, gelu, Y, bf16_out, ldy, st);
+}
+
+namespace {
+
+template <int kGS>
+hipError_t launch_grouped(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
+                          int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out, int64_t ldy,
+                          hipStream_t st) {
+#define QV_G(B, G, BIAS) \
+  launch_t<128, 128, 2, 2, 64, QV_STAGES, B, G, BIAS, false, kGS>(Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, st)
+  if (bias) {
+    if (bf16_out) return gelu ? QV_G(true, true, true) : QV_G(true, false, true);
+    return gelu ? QV_G(false, true, true) : QV_G(false, false, true);
+  }
+  if (bf16_out) return gelu ? QV_G(true, true, false) : QV_G(true, false, false);
+  return gelu ? QV_G(false, true, false) : QV_G(false, false, false);
+#undef QV_G
+}
+
+}  // namespace
+
+hipError_t launch_w4a4_gemm_grouped(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws,
+                                    const float* bias, int64_t M, int64_t N, int64_t K, int64_t group, bool gelu,
+                                    void* Y, bool bf16_out, int64_t ldy, hipStream_t st) {
+  if (group == 128) return launch_grouped<1>(Xq, xs, Wq, ws, bias, M, N, K, gelu, Y, bf16_out, ldy, st);
+  if (group == 256) return launch_grouped<2>(Xq, xs, Wq, ws, bias, M, N, K, gelu, Y, bf16_out, ldy, st);
+  return launch_grouped<4>(Xq, xs, Wq, ws, bias, M, N, K, gelu, Y, bf16_out, ldy, st);
 }
 
 hipError_t launch_w8a8_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,

@@ -31,6 +31,7 @@ class Layer:
     xs: object     # [M] fp32 activation scales
     Y: object      # [M][N] output
     bits: int = 4  # 4: packed int4 codes (W4A4); 8: int8 codes (W8A8)
+    group: int = 0  # > 0: group-wise scales over that many channels (ws [N][K/group], xs [M][K/group])
 
 
 def torch_dtype(name: str):
@@ -51,19 +52,23 @@ def run_linear(qv, L: Layer, stream=None) -> None:
     if L.bits == 8:
         qv.qv_hadamard_smooth_quant8(L.X, L.inv, L.Xq, L.xs, stream)
         qv.qv_w8a8_gemm(L.Xq, L.xs, L.Wq, L.ws, None, L.Y, L.lin.epi, stream)
+    elif L.group:
+        qv.qv_hadamard_smooth_quant_grouped(L.X, L.inv, L.group, L.Xq, L.xs, stream)
+        qv.qv_w4a4_gemm_grouped(L.Xq, L.xs, L.Wq, L.ws, None, L.Y, L.group, L.lin.epi, stream)
     else:
         qv.qv_hadamard_smooth_quant(L.X, L.inv, L.Xq, L.xs, stream)
         qv.qv_w4a4_gemm(L.Xq, L.xs, L.Wq, L.ws, None, L.Y, L.lin.epi, stream)
 
 
-def build(qv, wl: Workload, device, share_outputs: bool = False, bits: int = 4):
+def build(qv, wl: Workload, device, share_outputs: bool = False, bits: int = 4, group: int = 0):
     """Allocate and prepare every layer of ``wl`` on ``device`` (timing inputs, seeded on device).
 
     Activations are drawn per layer and per block.  With ``share_outputs`` the code/scale buffers
     and outputs are shared by the layers of equal shape across blocks (a 48-block stack would
     otherwise hold 48 copies of buffers that each step overwrites in order).  Weights are packed
     with ``qv_pack_weights`` (``qv_pack_weights8`` for ``bits=8``) after ``qv_smooth_calibrate`` on
-    frame 0 of the layer's input.
+    frame 0 of the layer's input.  ``group`` > 0 (4-bit codes) uses group-wise scales
+    (``qv_pack_weights_grouped``, ``qv_hadamard_smooth_quant_grouped``).
     """
     import torch
 
@@ -78,7 +83,7 @@ def build(qv, wl: Workload, device, share_outputs: bool = False, bits: int = 4):
         if share_outputs and key in shared:
             return shared[key]
         b = (torch.empty((M, row_codes(lin.K)), dtype=code_dt, device=device),
-             torch.empty((M,), dtype=torch.float32, device=device),
+             torch.empty((M, lin.K // group) if group else (M,), dtype=torch.float32, device=device),
              torch.empty((M, lin.N), dtype=out_dt, device=device))
         shared[key] = b
         return b
@@ -99,11 +104,14 @@ def build(qv, wl: Workload, device, share_outputs: bool = False, bits: int = 4):
                 calib = X[:synth.FRAME_TOKENS]
             qv.qv_smooth_calibrate(calib, W, s, inv, 0.5)
             Wq = torch.empty((lin.N, row_codes(lin.K)), dtype=code_dt, device=device)
-            ws = torch.empty((lin.N,), dtype=torch.float32, device=device)
-            (qv.qv_pack_weights8 if bits == 8 else qv.qv_pack_weights)(W, s, Wq, ws)
+            ws = torch.empty((lin.N, lin.K // group) if group else (lin.N,), dtype=torch.float32, device=device)
+            if group:
+                qv.qv_pack_weights_grouped(W, s, group, Wq, ws)
+            else:
+                (qv.qv_pack_weights8 if bits == 8 else qv.qv_pack_weights)(W, s, Wq, ws)
             del W
             Xq, xs, Y = buffers(lin)
-            L = Layer(lin, blk, X, inv, Wq, ws, Xq, xs, Y, bits)
+            L = Layer(lin, blk, X, inv, Wq, ws, Xq, xs, Y, bits, group)
             if chained:
                 L.X = prev.Y
             layers.append(L)
@@ -119,7 +127,7 @@ def frame0_output(qv, L: Layer, device):
     F = min(synth.FRAME_TOKENS, L.X.shape[0])
     tmp = Layer(L.lin, L.block, L.X[:F], L.inv, L.Wq, L.ws,
                 torch.empty((F, L.Xq.shape[1]), dtype=L.Xq.dtype, device=device),
-                torch.empty((F,), dtype=torch.float32, device=device),
-                torch.empty((F, L.lin.N), dtype=L.Y.dtype, device=device), L.bits)
+                torch.empty((F,) + tuple(L.xs.shape[1:]), dtype=torch.float32, device=device),
+                torch.empty((F, L.lin.N), dtype=L.Y.dtype, device=device), L.bits, L.group)
     run_linear(qv, tmp)
     return tmp.Y

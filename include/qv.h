@@ -166,6 +166,50 @@ qv_status qv_w8a8_linear(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, 
                          const float* bias, int64_t N, qv_epilogue epi, void* Y, qv_dtype y_dtype,
                          int64_t ldy, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/*
+ * Group-wise granularity ([P4] 双平滑细粒度量化（DSFQ） > 细粒度量化粒度; the subsection is truncated on
+ * the page).  Reading: the rotation and smoothing are unchanged (pre-global, over the whole row);
+ * each row of activations and of weights is quantized in groups of `group` consecutive channels
+ * of the rotated, smoothed row, each group with its own symmetric scale:
+ *   scale[r][g] = max_{k in group g} |Xt[r][k]| / 7,  q = clamp(rne(Xt / scale[r][g]), -8, 7)
+ * (a zero or subnormal group scale gives scale 0 and zero codes), and the product sums the groups'
+ * integer dot products, each dequantized by its own pair of scales:
+ *   Y[m][n] = sum_g (sum_{k in g} qa[m][k] qw[n][k]) * x_scale[m][g] * w_scale[n][g] (+ bias[n])
+ * (+ GELU), accumulated in fp32.  Codes use the int4 layout above; scales are row-major
+ * [rows][K / group] fp32.  group is 128, 256 or 512 and divides K, with K / group <= 32.
+ *
+ * qv_hadamard_smooth_quant_grouped / qv_pack_weights_grouped -- as qv_hadamard_smooth_quant /
+ *   qv_pack_weights (same arguments and rules, K in {1024, 4096}), writing x_scale [M][K / group]
+ *   / w_scale [N][K / group].  An unsupported group returns QV_ERR_UNSUPPORTED.
+ */
+qv_status qv_hadamard_smooth_quant_grouped(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                           const float* inv_smooth, int64_t group, uint8_t* Xq, float* x_scale,
+                                           void* hip_stream);
+qv_status qv_pack_weights_grouped(const void* W, qv_dtype w_dtype, int64_t N, int64_t K, int64_t ldw,
+                                  const float* smooth, int64_t group, uint8_t* Wq, float* w_scale,
+                                  void* hip_stream);
+
+/*
+ * qv_w4a4_gemm_grouped -- the int4 x int4 contraction with group-wise dequantization: each
+ * group's int32 dot products (exact) times x_scale[m][g] w_scale[n][g], summed over the groups in
+ * fp32, then bias and GELU as in qv_w4a4_gemm.  x_scale [M][K / group], w_scale [N][K / group];
+ * other arguments and rules as for qv_w4a4_gemm.
+ */
+qv_status qv_w4a4_gemm_grouped(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq, const float* w_scale,
+                               const float* bias, int64_t M, int64_t N, int64_t K, int64_t group, qv_epilogue epi,
+                               void* Y, qv_dtype y_dtype, int64_t ldy, void* hip_stream);
+
+/* Workspace of qv_w4a4_linear_grouped: M*K/2 code bytes and 4*M*(K/group) scale bytes, each
+ * rounded up to 256 bytes (0 for invalid sizes). */
+size_t qv_w4a4_linear_grouped_workspace_size(int64_t M, int64_t K, int64_t group);
+
+/* qv_w4a4_linear_grouped -- qv_hadamard_smooth_quant_grouped into the workspace, then
+ * qv_w4a4_gemm_grouped; arguments and workspace rules as for qv_w4a4_linear. */
+qv_status qv_w4a4_linear_grouped(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                 const float* inv_smooth, int64_t group, const uint8_t* Wq, const float* w_scale,
+                                 const float* bias, int64_t N, qv_epilogue epi, void* Y, qv_dtype y_dtype,
+                                 int64_t ldy, void* workspace, size_t workspace_bytes, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

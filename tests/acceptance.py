@@ -118,3 +118,68 @@ def check_outputs(y_gpu, y_ref, out_bf16: bool, label=""):
     worst = float(np.max(rel)) if rel.size else 0.0
     assert worst <= OUT_REL_MAX, f"{label}: max relative error {worst:.3e} > {OUT_REL_MAX}"
     return worst
+
+
+# ------------------------------------------------------------------ group-wise granularity
+# The same bounds with one scale per row and group of channels: the butterfly error of an element
+# is the row's (the rotation is over the whole row), the scale is its group's.
+
+def code_bounds_grouped(X, mult, group: int, Xhat=None, qmax: int = 7):
+    """t, tau (as code_bounds) and the per-(row, group) scales and relative scale tolerances."""
+    X = np.asarray(X, dtype=np.float64)
+    M, K = X.shape
+    G = K // group
+    if Xhat is None:
+        Xhat = oracle.rotate(X, oracle.ROT_FWHT)
+    m = np.ones(K) if mult is None else np.asarray(mult, dtype=np.float64)
+    L = math.log2(K)
+    xt = Xhat * m
+    a = np.max(np.abs(xt).reshape(M, G, group), axis=2)
+    flushed = (np.max(np.abs(Xhat.astype(np.float32) * m.astype(np.float32)).reshape(M, G, group), axis=2)
+               / np.float32(qmax)) < FLT_MIN32
+    s = np.where(flushed, 0.0, a / float(qmax))
+    se = np.repeat(s, group, axis=1)
+    mmax = np.max(np.abs(m).reshape(G, group), axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(se > 0, xt / se, 0.0)
+        e_x = L * U * np.sum(np.abs(X), axis=1) / math.sqrt(K)
+        rel_scale = np.where(a > 0, e_x[:, None] * mmax[None, :] / a, 0.0) + 4 * U
+        tau = 2.0 * ((e_x[:, None] * np.abs(m)[None, :] + 2 * U * np.abs(xt)) / np.where(se > 0, se, 1.0)
+                     + np.abs(t) * np.repeat(rel_scale, group, axis=1))
+    return t, tau, s, rel_scale
+
+
+def grouped_abs_sum(qa, qw, sa, sw):
+    """sum_g |acc_g| sa[:, g] sw[:, g] (fp64) from int8 codes: the size of the terms the fp32
+    accumulation of a grouped product adds up."""
+    qa = np.asarray(qa, dtype=np.int8)
+    qw = np.asarray(qw, dtype=np.int8)
+    K = qa.shape[1]
+    G = sa.shape[1]
+    group = K // G
+    out = np.zeros((qa.shape[0], qw.shape[0]))
+    for g in range(G):
+        sl = slice(g * group, (g + 1) * group)
+        acc = oracle.gemm_int(qa[:, sl], qw[:, sl]).astype(np.float64)
+        out += np.abs(acc) * sa[:, g:g + 1].astype(np.float64) * sw[:, g].astype(np.float64)[None, :]
+    return out
+
+
+def check_outputs_grouped(y_gpu, y_ref, y_abs, out_bf16: bool, groups: int, label=""):
+    """Grouped outputs: each group adds one product and one fp32 sum to the accumulator, so beyond
+    the relative bar of check_outputs an absolute (groups + 3) * 2u * sum_g |term_g| is allowed
+    (x 1.2 for the GELU's slope).  Returns the worst error in units of the allowance."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    extra = 1.2 * 2.0 * (groups + 3) * U * np.asarray(y_abs, dtype=np.float64)
+    if out_bf16:
+        r = bf16_round(y_ref)
+        allow = np.abs(r) * 2.0 ** -7 + extra + 1e-38
+        err = np.abs(y_gpu - r)
+    else:
+        allow = OUT_REL_MAX * np.abs(y_ref) + extra + float(FLT_MIN32)
+        err = np.abs(y_gpu - y_ref)
+    bad = err > allow
+    assert not np.any(bad), (f"{label}: {int(bad.sum())} outputs beyond the bound, e.g. "
+                             f"{[(float(y_gpu[tuple(i)]), float(y_ref[tuple(i)])) for i in np.argwhere(bad)[:3]]}")
+    return float(np.max(err / allow)) if err.size else 0.0

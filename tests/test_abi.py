@@ -172,3 +172,31 @@ def test_w8a8_argument_errors(L):
     need = L.qv_w8a8_linear_workspace_size(16, 1024)
     assert L.qv_w8a8_linear(P, 0, 16, 1024, 1024, None, P, P, None, 128, 0, P, 0, 128, P, need - 1, None) == \
         QV_ERR_WORKSPACE
+
+
+def test_grouped_argument_errors(L):
+    """Group sizes other than 128, 256 and 512, groups not dividing K, or more than 32 groups per
+    row are rejected before any launch; the rest follows the per-token rules."""
+    def hsqg(group=128, M=16, K=1024, X=P):
+        return L.qv_hadamard_smooth_quant_grouped(X, 0, M, K, K, None, group, P, P, None)
+
+    def gg(group=128, K=1024, M=16, Xq=P):
+        return L.qv_w4a4_gemm_grouped(Xq, P, P, P, None, M, 128, K, group, 0, P, 0, 128, None)
+
+    assert hsqg(M=0) == QV_OK
+    assert hsqg(group=64) == QV_ERR_UNSUPPORTED
+    assert hsqg(group=1024) == QV_ERR_UNSUPPORTED
+    assert hsqg(X=None) == QV_ERR_NULL
+    assert L.qv_pack_weights_grouped(P, 0, 8, 4096, 4096, None, 96, P, P, None) == QV_ERR_UNSUPPORTED
+    assert gg(M=0) == QV_OK
+    assert gg(group=100) == QV_ERR_UNSUPPORTED
+    assert gg(K=1152, group=256) == QV_ERR_UNSUPPORTED   # 256 does not divide 1152
+    assert gg(K=8192, group=128) == QV_ERR_UNSUPPORTED   # 64 groups per row
+    assert gg(Xq=None) == QV_ERR_NULL
+    assert L.qv_w4a4_linear_grouped_workspace_size(1374, 1024, 128) == 1374 * 512 + ((1374 * 8 * 4 + 255) // 256) * 256
+    assert L.qv_w4a4_linear_grouped_workspace_size(10, 1024, 96) == 0
+    need = L.qv_w4a4_linear_grouped_workspace_size(16, 1024, 256)
+    assert L.qv_w4a4_linear_grouped(P, 0, 16, 1024, 1024, None, 256, P, P, None, 128, 0, P, 0, 128, P, need - 1,
+                                    None) == QV_ERR_WORKSPACE
+    assert L.qv_w4a4_linear_grouped(P, 0, 16, 1024, 1024, None, 384, P, P, None, 128, 0, P, 0, 128, P, need,
+                                    None) == QV_ERR_UNSUPPORTED
