@@ -42,7 +42,7 @@ def parse_args():
                    help="a second workload timed the same way after the main one ('' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
     p.add_argument("--no-bf16-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=256, help="rows per linear in the oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=384, help="rows per linear in the oracle sample (about 10 s of host work)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="before the timed steps, copy this many MiB device-to-device once (a plain copy "
                         "of known size that calibrates the HBM byte counters of a profiling run)")
