@@ -14,7 +14,7 @@
 //     u ^ ((r ^ r >> 2) & 3)) so the fragment reads hit distinct banks;
 //   * a fragment is two ds_read_b128 per lane (32 + 32 packed codes), feeding four MFMAs;
 //   * codes are widened to int8 with two masks: (p & 0xF0F0F0F0) keeps the odd-k nibbles as 16 q
-//     and ((p << 4) & 0xF0F0F0F0) the even-k ones.  Both operands carry the factor 16, so the
+//     and ((p << 4) & 0xF0F0F0F0) the even-k ones (the shift done for two dwords at once).  Both operands carry the factor 16, so the
 //     accumulator holds 256 * acc (exact: |256 acc| <= 256 * 64 * 65536 < 2^31); the epilogue
 //     folds the 2^-8 into the row scale.  A and B are widened the same way, so every k is paired
 //     with itself and the order of the terms inside a fragment does not matter;
@@ -91,11 +91,16 @@ __device__ __forceinline__ int swz(int r) {
   return (U == 4) ? ((r ^ (r >> 2)) & 3) : ((r ^ (r >> 3)) & 7);
 }
 
+// The even-k nibbles of both packed dwords are shifted by one 64-bit shift (the bits carried from
+// p0 into p1's low nibble are masked off with the rest); written directly, because the compiler
+// splits a 64-bit shift whose carried bits are masked into two 32-bit shifts.
 __device__ __forceinline__ v4i widen(uint32_t p0, uint32_t p1) {
+  uint64_t w = (((uint64_t)p1) << 32) | p0;
+  asm("v_lshlrev_b64 %0, 4, %1" : "=v"(w) : "v"(w));
   v4i o;
-  o[0] = (int)((p0 << 4) & 0xF0F0F0F0u);
+  o[0] = (int)((uint32_t)w & 0xF0F0F0F0u);
   o[1] = (int)(p0 & 0xF0F0F0F0u);
-  o[2] = (int)((p1 << 4) & 0xF0F0F0F0u);
+  o[2] = (int)((uint32_t)(w >> 32) & 0xF0F0F0F0u);
   o[3] = (int)(p1 & 0xF0F0F0F0u);
   return o;
 }
