@@ -5,27 +5,30 @@
 // QuantVGGT paper) with symmetric per-token / per-output-channel scales ("十亿参数的三维重建模型，
 // 能塞进手机吗？" (gslzct.com), 训练后量化（PTQ）), so y = acc * x_scale[m] * w_scale[n].
 //
-// Block tile BN (weight rows n) x BM (token rows m), four waves in a 2 x 2 grid; each wave owns a
-// (BN/2) x (BM/2) sub-tile of v_mfma_i32_32x32x32_i8 fragments whose int32 accumulators live in
-// the AGPR file.  Per stage of 128 codes (64 bytes of every tile row):
+// Block tile BN (weight rows n) x BM (token rows m) over a WGN x WGM grid of waves (2 x 2 by
+// default); each wave owns a (BN/WGN) x (BM/WGM) sub-tile of v_mfma_i32_32x32x32_i8 fragments whose
+// int32 accumulators stay in registers.  Per stage of 128 codes (64 bytes of every tile row):
 //   * each wave issues global_load_lds_dwordx4 for its share of both packed tiles (no registers,
 //     no LDS store instructions) into a ring of STAGES buffers, STAGES - 1 stages ahead; the
 //     16-byte units of a 64-byte tile row are stored XOR-swizzled (unit u of row r at
 //     u ^ ((r ^ r >> 2) & 3)) so the fragment reads hit distinct banks;
 //   * a fragment is two ds_read_b128 per lane (32 + 32 packed codes), feeding four MFMAs;
 //   * codes are widened to int8 with two masks: (p & 0xF0F0F0F0) keeps the odd-k nibbles as 16 q
-//     and ((p << 4) & 0xF0F0F0F0) the even-k ones (the shift done for two dwords at once).  Both operands carry the factor 16, so the
-//     accumulator holds 256 * acc (exact: |256 acc| <= 256 * 64 * 65536 < 2^31); the epilogue
-//     folds the 2^-8 into the row scale.  A and B are widened the same way, so every k is paired
-//     with itself and the order of the terms inside a fragment does not matter;
-//   * the widening of the next operands is interleaved with the MFMAs (three VALU ops per MFMA), so
-//     the unpack runs on the vector ALU while the matrix core is busy.
+//     and ((p << 4) & 0xF0F0F0F0) the even-k ones (one 64-bit shift serves two dwords).  Both
+//     operands carry the factor 16, so the accumulator holds 256 * acc (exact: |256 acc| <=
+//     256 * 64 * 65536 < 2^31); the epilogue folds the 2^-8 into the row scale.  A and B are
+//     widened the same way, so every k is paired with itself and the order of the terms inside a
+//     fragment does not matter;
+//   * the widening of the next operands is interleaved with the MFMAs, so the unpack runs on the
+//     vector ALU while the matrix core is busy.
 // The tile's row and column scales are fetched into LDS by LDS-DMA when the tile starts, so the
-// epilogue does not wait on global memory.
+// epilogue does not wait on global memory.  With group-wise scales (kGS > 0) each group's int32
+// accumulators are dequantized into fp32 accumulators after the group's last stage.
 // MFMA operand roles: A = weight tile (output rows i = n), B = activation tile (columns j = m): a
-// lane owns runs of four consecutive n of one m and writes each with one 8-byte (bf16) or 16-byte
-// (fp32) store.  Tiles are assigned XCD-major: the hardware deals blocks round-robin over the 8
-// XCDs, and the block -> tile map gives each XCD a contiguous run of tiles sharing activation rows.
+// lane owns runs of four consecutive n of one m; the epilogue stages each wave's outputs in LDS and
+// writes whole 128-byte row segments with 16-byte stores.  Tiles are assigned XCD-major: the
+// hardware deals blocks round-robin over the 8 XCDs, and the block -> tile map gives each XCD a
+// contiguous run of tiles sharing activation rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
