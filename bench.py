@@ -246,6 +246,36 @@ def main():
                                    "w4a4_speedup": round(bt / (wall / args.steps), 3)}
         del base
 
+        # hipBLASLt's int8 GEMM on the same shapes (int8 operands, int32 output, no scales): the
+        # vendor library's contraction alone, against this GEMM with its unpack and epilogue.
+        i8 = []
+        for L in layers[:len(wl.linears)]:
+            lin = L.lin
+            g = torch.Generator(device=dev).manual_seed(lin.x_seed)
+            A = torch.randint(-8, 8, (M, lin.K), dtype=torch.int8, device=dev, generator=g)
+            Bt = torch.randint(-8, 8, (lin.N, lin.K), dtype=torch.int8, device=dev, generator=g)
+            i8.append((A, Bt.t()))
+
+        def istep():
+            for A, B in i8:
+                torch._int_mm(A, B)
+        try:
+            for _ in range(args.warmup):
+                istep()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                for _ in range(wl.blocks):
+                    istep()
+            torch.cuda.synchronize()
+            it = (time.perf_counter() - t0) / args.steps
+            result["int8_baseline"] = {"what": "torch._int_mm (hipBLASLt int8 x int8 -> int32, no scales), same shapes",
+                                       "TOPS": round(ops_per_step / it / 1e12, 2),
+                                       "w4a4_gemm_speedup": round(k2_tops / (ops_per_step / it / 1e12), 3)}
+        except RuntimeError as e:  # an int8 GEMM the installed torch does not offer on this device
+            result["int8_baseline"] = {"what": "torch._int_mm", "error": str(e)[:200]}
+        del i8
+
     # ---------------------------------------------------------------- CPU oracle on a bounded sample
     if not args.no_cpu_baseline:
         import oracle
