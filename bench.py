@@ -72,8 +72,8 @@ def read_traffic(kernel_tag, src_hash):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
-                          "requested_gpus": args.gpus}))
+        print(json.dumps({"error": "the benchmark times the path on one GPU (token rows shard across GPUs "
+                                   "with no exchange); --gpus must be 1", "requested_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np
