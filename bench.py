@@ -69,6 +69,47 @@ def read_traffic(kernel_tag, src_hash):
     return d.get("bytes_per_launch")
 
 
+def sample_clock(step, torch):
+    """Graphics clock while the steps keep running (after the timed region, so the sampling does
+    not share it): the median of a few reads of the current DPM level's frequency in sysfs
+    (pp_dpm_sclk, the line marked '*'); None where that file is not readable."""
+    import glob
+    import threading
+
+    files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not files:
+        return None
+
+    def read_mhz():
+        for f in files:
+            try:
+                for line in open(f):
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    samples = []
+
+    def sampler():
+        time.sleep(0.2)  # let the steps reach their steady clock
+        for _ in range(5):
+            v = read_mhz()
+            if v is not None:
+                samples.append(v)
+            time.sleep(0.05)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    while th.is_alive():
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    th.join()
+    return float(sorted(samples)[len(samples) // 2]) if samples else None
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -121,6 +162,7 @@ def main():
 
     ops_per_step = sum(2.0 * M * L.lin.N * L.lin.K for L in layers)
     value = ops_per_step / (wall / args.steps) / 1e12
+    sclk = sample_clock(step, torch)
 
     # ---------------------------------------------------------------- per-kernel times (HIP events)
     # Events on the library's stream bracket back-to-back launches with no event between them (an
@@ -203,7 +245,9 @@ def main():
         "roofline": {"kernel": "w4a4_gemm", "bound": "mfma", "achieved": round(k2_tops, 2),
                      "peak": PEAK_INT8_TOPS, "unit": "TOP/s", "frac": round(k2_tops / PEAK_INT8_TOPS, 4),
                      "traffic": read_traffic("w4a4_gemm", gemm_hash),
-                     "avg_launch_us": round(1e6 * k2_t, 3), "ops_per_launch": k2_ops},
+                     "avg_launch_us": round(1e6 * k2_t, 3), "ops_per_launch": k2_ops,
+                     "frac_at_sampled_clock": (round(k2_tops / (PEAK_INT8_TOPS * sclk / 2400.0), 4)
+                                               if sclk else None)},
         "rotate_quant_roofline": {"kernel": "rotate_quant", "bound": "hbm", "achieved": round(k1_gbps, 1),
                                   "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(k1_gbps / PEAK_HBM_GBPS, 4),
                                   "traffic": read_traffic("rotate_quant", rq_hash),
@@ -212,6 +256,7 @@ def main():
         "kernels": kernels,
         "rotate_quant_share_of_linear_time": round(k1_t / (k1_t + k2_t), 4),
         "kernel_timing": f"HIP events around {reps} back-to-back repetitions of every layer's launch of the kernel",
+        "gfx_clock_MHz_under_load": sclk,
         "weights_resident": {"int4_bytes_with_scales": wq_bytes, "bf16_bytes": bf16_w_bytes,
                              "ratio": round(bf16_w_bytes / wq_bytes, 3)},
         "gemm_only_TOPS": round(k2_tops, 2),
