@@ -195,7 +195,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // The wave index is uniform; readfirstlane keeps it (and the LDS-DMA addresses derived from it)
+  // in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % WGN, wm = wave / WGN;
 
   // XCD-major tile order.
@@ -215,27 +217,34 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
 
   // Source of each of this lane's loads; LDS unit P = 64 * (kWaves i + wave) + lane of the stage
   // buffer.
-  const uint8_t* src[kLoads];
+  // Each load instruction covers 16 whole tile rows, so it reads either the weight tile or the
+  // activation tile: a uniform base (that tile's first row) plus a per-lane 32-bit offset.
+  static_assert((BN * U) % 64 == 0, "a load instruction stays inside one operand tile");
+  const uint8_t* sbase[kLoads];
+  uint32_t soff[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const int P = 64 * (kWaves * i + wave) + lane;
     const int r = P / U;  // row inside the combined A|B tile
-    if (r < BN) {
-      src[i] = Wq + (n0 + r) * row_bytes + 16 * ((P % U) ^ swz<U>(r));
+    if (64 * (kWaves * i + wave) < BN * U) {
+      sbase[i] = Wq + n0 * row_bytes;
+      soff[i] = (uint32_t)(r * row_bytes + 16 * ((P % U) ^ swz<U>(r)));
     } else {
       const int rb = r - BN;
       int64_t mr = m0 + rb;
       if (mr > M - 1) mr = M - 1;  // ragged tail: repeat the last row; its outputs are not stored
-      src[i] = Xq + mr * row_bytes + 16 * ((P % U) ^ swz<U>(rb));
+      sbase[i] = Xq + m0 * row_bytes;
+      soff[i] = (uint32_t)((mr - m0) * row_bytes + 16 * ((P % U) ^ swz<U>(rb)));
     }
   }
+  auto src_at = [&](int i, int64_t kb) { return sbase[i] + kb + soff[i]; };
   // Stage loads.  With LDS-DMA (global_load_lds_dwordx4) the 16 bytes of lane l land at unit
   // 64 * (kWaves i + wave) + l of the stage buffer directly; otherwise they are fetched into registers
   // (fetch_stage) and written to the same units with ds_write_b128 (store_stage).
   u32x4 staged[kLoads];
   auto fetch_stage = [&](int64_t kb) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) staged[i] = *reinterpret_cast<const u32x4*>(src[i] + kb);
+    for (int i = 0; i < kLoads; ++i) staged[i] = *reinterpret_cast<const u32x4*>(src_at(i, kb));
   };
   auto store_stage = [&](int buf) {
 #pragma unroll
@@ -246,7 +255,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       uint8_t* dst = lds + buf * kStageBytes + 1024 * (kWaves * i + wave);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[i] + kb),
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src_at(i, kb)),
                                        reinterpret_cast<__attribute__((address_space(3))) void*>(
                                            reinterpret_cast<uintptr_t>(dst)),
                                        16, 0, 0);
@@ -304,7 +313,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
 
   // One stage: wait for stage kt, refill the ring, read and widen the fragments, 16 MFMAs.  A
   // "fresh" stage starts its accumulators from zero (the first stage of a group of channels).
-  auto stage_step = [&](int kt, auto fresh) {
+  auto stage_step = [&](int kt, auto fresh, int buf) {  // buf = kt % STAGES
     constexpr bool kFresh = decltype(fresh)::value;
     if constexpr (QV_DMA) {
       // Stage kt has landed once at most STAGES - 2 later stages are still in flight.
@@ -313,13 +322,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
     }
     __syncthreads();  // every wave's share of stage kt is in LDS; stage kt - 1 is consumed
     const bool refill = kt + STAGES - 1 < nk;
+    const int rbuf = buf == 0 ? STAGES - 1 : buf - 1;  // (kt + STAGES - 1) % STAGES
     if constexpr (QV_DMA) {
-      if (refill) issue_stage((kt + STAGES - 1) % STAGES, (int64_t)(kt + STAGES - 1) * kRowBytes);
+      if (refill) issue_stage(rbuf, (int64_t)(kt + STAGES - 1) * kRowBytes);
     } else {
       if (refill) fetch_stage((int64_t)(kt + STAGES - 1) * kRowBytes);
     }
 
-    const uint8_t* As = lds + (kt % STAGES) * kStageBytes;
+    const uint8_t* As = lds + buf * kStageBytes;
     const uint8_t* Bs = As + BN * kRowBytes;
     u32x4 pa[FN][kReads], pb[FM][kReads];
 #pragma unroll
@@ -379,7 +389,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
     if constexpr (!QV_DMA) {
       // The buffer of stage kt + STAGES - 1 held stage kt - 1, which every wave finished reading
       // before this iteration's barrier.
-      if (refill) store_stage((kt + STAGES - 1) % STAGES);
+      if (refill) store_stage(rbuf);
     }
   };
 
@@ -392,14 +402,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
   }
   (void)facc;
   if constexpr (kGS == 0) {
-    for (int kt = 0; kt < nk; ++kt) stage_step(kt, std::false_type{});
+    for (int kt = 0; kt < nk; ++kt) stage_step(kt, std::false_type{}, kt % STAGES);
   } else {
     // Groups of kGS stages; after each, acc (256 x the group's integer dot products) is
     // dequantized with the group's scales into facc: the row scale carries the 2^-8.
     for (int kt0 = 0; kt0 < nk; kt0 += kGS) {
-      stage_step(kt0, std::true_type{});
+      stage_step(kt0, std::true_type{}, kt0 % STAGES);
 #pragma unroll
-      for (int st = 1; st < kGS; ++st) stage_step(kt0 + st, std::false_type{});
+      for (int st = 1; st < kGS; ++st) stage_step(kt0 + st, std::false_type{}, (kt0 + st) % STAGES);
       const float* sg = scales + (kt0 / kGS) * (BN + BM);
 #pragma unroll
       for (int c = 0; c < FM; ++c) {
