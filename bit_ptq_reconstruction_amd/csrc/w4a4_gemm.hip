@@ -8,8 +8,9 @@
 // Block tile BN (weight rows n) x BM (token rows m) over a WGN x WGM grid of waves (2 x 2 by
 // default); each wave owns a (BN/WGN) x (BM/WGM) sub-tile of v_mfma_i32_32x32x32_i8 fragments whose
 // int32 accumulators stay in registers.  Per stage of 128 codes (64 bytes of every tile row):
-//   * each wave issues global_load_lds_dwordx4 for its share of both packed tiles (no registers,
-//     no LDS store instructions) into a ring of STAGES buffers, STAGES - 1 stages ahead; the
+//   * each wave issues LDS-DMA loads (buffer_load_dwordx4 ... lds, the stage offset in a scalar
+//     register) for its share of both packed tiles (no registers, no LDS store instructions) into
+//     a ring of STAGES buffers, STAGES - 1 stages ahead; the
 //     16-byte units of a 64-byte tile row are stored XOR-swizzled (unit u of row r at
 //     u ^ ((r ^ r >> 2) & 3)) so the fragment reads hit distinct banks;
 //   * a fragment is two ds_read_b128 per lane (32 + 32 packed codes), feeding four MFMAs;
@@ -60,6 +61,12 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #endif
 
 constexpr int kXcds = 8;
+
+#ifndef QV_BUF_DMA
+#define QV_BUF_DMA 1  // 1: stage loads through buffer resources (scalar stage offset); 0: global addresses
+#endif
+// Word 3 of a raw buffer resource on gfx9-class GPUs (32-bit data format, no swizzle).
+constexpr int kBufDword3 = 0x00020000;
 
 // Position inside an XCD's run -> offset in the run's canonical (row-major over tiles) order.
 // G = 0 keeps the canonical order: the blocks in flight share a few activation rows and sweep every
@@ -238,6 +245,22 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
     }
   }
   auto src_at = [&](int i, int64_t kb) { return sbase[i] + kb + soff[i]; };
+  // Buffer resources over the two operand tiles (raw, byte-addressed): a stage's loads then take
+  // the lane offset in a vector register and the stage's byte offset kb in a scalar one, so no
+  // vector instruction advances an address from stage to stage.
+  // (The host pass does not know the buffer-resource type; it compiles the global-address form.)
+#if defined(__HIP_DEVICE_COMPILE__)
+  __amdgpu_buffer_rsrc_t rsrc[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const bool isA = 64 * (kWaves * i + wave) < BN * U;
+    rsrc[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sbase[i]), (short)0,
+                                                (int)((isA ? BN : BM) * row_bytes), kBufDword3);
+  }
+  constexpr bool kBufDma = QV_BUF_DMA;
+#else
+  constexpr bool kBufDma = false;
+#endif
   // Stage loads.  With LDS-DMA (global_load_lds_dwordx4) the 16 bytes of lane l land at unit
   // 64 * (kWaves i + wave) + l of the stage buffer directly; otherwise they are fetched into registers
   // (fetch_stage) and written to the same units with ds_write_b128 (store_stage).
@@ -255,10 +278,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       uint8_t* dst = lds + buf * kStageBytes + 1024 * (kWaves * i + wave);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src_at(i, kb)),
-                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                           reinterpret_cast<uintptr_t>(dst)),
-                                       16, 0, 0);
+      auto* ldst = reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(dst));
+      if constexpr (kBufDma) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc[i], ldst, 16, soff[i], (unsigned)kb, 0, 0);
+#endif
+      } else {
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src_at(i, kb)), ldst, 16, 0, 0);
+      }
     }
   };
   (void)fetch_stage; (void)store_stage; (void)issue_stage;
