@@ -162,7 +162,9 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const In* __rest
   using L = RowLayout<K>;
   __shared__ __attribute__((aligned(16))) float cm_lds[(K == 1024 ? 16 : 64) * kCmStride];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // The wave index, hence the row group, is uniform; readfirstlane keeps the group's addresses in
+  // scalar registers, and each lane adds a 32-bit offset.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane / L::kLanesPerRow;  // row inside the wave
   const float* cm_row = cm_lds + (K == 1024 ? (lane & 15) : lane) * kCmStride;
 
@@ -172,13 +174,15 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const In* __rest
 
   // Rows past the end are clamped to the last row (loaded, transformed, never stored), so every
   // load is unconditional and no lane diverges before the stores.
-  auto row_of = [&](int64_t grp) {
-    const int64_t r = grp * L::kRowsPerWave + sub;
-    return r < M ? r : M - 1;
+  // The lane's row as (uniform first row of the group) + (row inside the group, clamped).
+  auto row_ptr = [&](int64_t grp) {
+    const int64_t r0 = grp * L::kRowsPerWave;
+    const int64_t r = r0 + sub < M ? r0 + sub : M - 1;
+    return X + r0 * ldx + (uint32_t)((r - r0) * ldx);
   };
 #if QV_RQ_PREFETCH
   RawRow<In> next;
-  if (g < groups) load_raw<K, In>(X + row_of(g) * ldx, lane, next);
+  if (g < groups) load_raw<K, In>(row_ptr(g), lane, next);
 #endif
 
   fill_multiplier_table<K>(mult, cm_lds);
@@ -190,9 +194,9 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const In* __rest
 #if QV_RQ_PREFETCH
     unpack_raw<In>(next, v);
     // Prefetch the next row group while this one is transformed.
-    if (g + wave_stride < groups) load_raw<K, In>(X + row_of(g + wave_stride) * ldx, lane, next);
+    if (g + wave_stride < groups) load_raw<K, In>(row_ptr(g + wave_stride), lane, next);
 #else
-    load_row<K, In>(X + row_of(g) * ldx, lane, v);
+    load_row<K, In>(row_ptr(g), lane, v);
 #endif
 
     fwht_row_regs<K>(v, lane);
@@ -250,10 +254,11 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const In* __rest
 #pragma unroll
         for (int e = 0; e < 8; ++e) m[e] = __builtin_bit_cast(uint32_t, __builtin_fmaf(v[j][e], rg[j], kMagic<kBits>));
         // the lane's eight codes of group j are k = 8 dword_index + 0..7
+        uint8_t* const qrow = Xq + g * L::kRowsPerWave * (K * kBits / 8) + (uint32_t)(sub * (K * kBits / 8));
         if constexpr (kBits == 4) {
-          reinterpret_cast<uint32_t*>(Xq + row * (K / 2))[dword_index<K>(lane, j)] = pack8(m);
+          reinterpret_cast<uint32_t*>(qrow)[dword_index<K>(lane, j)] = pack8(m);
         } else {
-          reinterpret_cast<uint2*>(Xq + row * K)[dword_index<K>(lane, j)] = pack8_int8(m);
+          reinterpret_cast<uint2*>(qrow)[dword_index<K>(lane, j)] = pack8_int8(m);
         }
       }
       if constexpr (kGroup == 0) {
