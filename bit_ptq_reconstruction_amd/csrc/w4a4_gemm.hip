@@ -470,13 +470,21 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
   for (int c = 0; c < FM; ++c) sa[c] = scales[BN + wm * WM + 32 * c + r32] * (kW8 ? 1.0f : 0.00390625f);
   // y for fragment (a, c) and register group vg: the lane's four consecutive columns
   // n = wn*WN + 32a + 8vg + 4h + (0..3) of row m = wm*WM + 32c + r32, dequantized (+ bias) (+ GELU).
+  // The lane's weight scales are read once, before the staging passes, so the passes' LDS writes
+  // and reads do not wait behind scale reads.
+  float4 sw4[FN][4];
+#pragma unroll
+  for (int a = 0; a < FN; ++a)
+#pragma unroll
+    for (int vg = 0; vg < 4; ++vg)
+      if constexpr (kGS == 0) sw4[a][vg] = *reinterpret_cast<const float4*>(scales + wn * WN + 32 * a + 8 * vg + 4 * h);
+  (void)sw4;
   auto outputs = [&](int a, int c, int vg, float (&y)[4]) {
-    const int nl = 32 * a + 8 * vg + 4 * h;
-    const float4 sw4 = *reinterpret_cast<const float4*>(scales + wn * WN + nl);
-    const float sw[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
+    float sw[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kGS == 0) { sw[0] = sw4[a][vg].x; sw[1] = sw4[a][vg].y; sw[2] = sw4[a][vg].z; sw[3] = sw4[a][vg].w; }
     float bb[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (kBias) {
-      const float4 b4 = *reinterpret_cast<const float4*>(bias + n0 + wn * WN + nl);
+      const float4 b4 = *reinterpret_cast<const float4*>(bias + n0 + wn * WN + 32 * a + 8 * vg + 4 * h);
       bb[0] = b4.x; bb[1] = b4.y; bb[2] = b4.z; bb[3] = b4.w;
     }
 #pragma unroll
