@@ -1,6 +1,7 @@
 /*
  * qv.h -- C ABI of libqv, an MI355X (gfx950) library for the W4A4 Hadamard-rotated, smoothed,
- * int4-quantized linear layer of QuantVGGT (and its W8A8 variant, at the end of this file).
+ * int4-quantized linear layer of QuantVGGT (and, at the end of this file, its W8A8 variant and a
+ * variant with group-wise scales).
  *
  * Sources, cited by page title and section:
  *   [P4] "十亿参数的三维重建模型，能塞进手机吗？" (gslzct.com), a translation of the QuantVGGT
