@@ -20,8 +20,9 @@
 //     256 * 64 * 65536 < 2^31); the epilogue folds the 2^-8 into the row scale.  A and B are
 //     widened the same way, so every k is paired with itself and the order of the terms inside a
 //     fragment does not matter;
-//   * the widening of the next operands is interleaved with the MFMAs, so the unpack runs on the
-//     vector ALU while the matrix core is busy.
+//   * the widening of the next operands is interleaved with the MFMAs (the compiler's schedule),
+//     so the unpack runs on the vector ALU while the matrix core is busy; the K loop is unrolled
+//     by the ring depth, so a stage's LDS read addresses are instruction offsets.
 // The tile's row and column scales are fetched into LDS by LDS-DMA when the tile starts, so the
 // epilogue does not wait on global memory.  With group-wise scales (kGS > 0) each group's int32
 // accumulators are dequantized into fp32 accumulators after the group's last stage.
@@ -402,16 +403,6 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
           for (int a = 0; a < FN; ++a) acc[a][c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[a], fb, (kFresh && s == 0) ? v16i{} : acc[a][c], 0, 0, 0);
         }
       }
-      // Schedule: the fragment reads, the first sub-step's widening, then one MFMA per three VALU
-      // ops so the remaining widening overlaps the matrix core.
-      __builtin_amdgcn_sched_group_barrier(0x100, kReads * (FN + FM), 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6 * (FN + FM), 0);
-#pragma unroll
-      for (int i = 0; i < 2 * (kSub - 1) * (FN + FM); ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kSub * FN * FM - 2 * (kSub - 1) * (FN + FM), 0);
     }
     if constexpr (!QV_DMA) {
       // The buffer of stage kt + STAGES - 1 held stage kt - 1, which every wave finished reading
@@ -429,7 +420,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
   }
   (void)facc;
   if constexpr (kGS == 0) {
-    for (int kt = 0; kt < nk; ++kt) stage_step(kt, std::false_type{}, kt % STAGES);
+    // Whole turns of the ring first, so each step's buffer index is a constant and its LDS
+    // addresses become instruction offsets; then the remaining stages.
+    int kt = 0;
+    for (; kt + STAGES <= nk; kt += STAGES) {
+#pragma unroll
+      for (int b = 0; b < STAGES; ++b) stage_step(kt + b, std::false_type{}, b);
+    }
+    for (; kt < nk; ++kt) stage_step(kt, std::false_type{}, kt % STAGES);
   } else {
     // Groups of kGS stages; after each, acc (256 x the group's integer dot products) is
     // dequantized with the group's scales into facc: the row scale carries the 2^-8.
