@@ -40,6 +40,8 @@ qv_status check_gemm(const void* Xq, const float* xs, const void* Wq, const floa
   if (M < 0 || N < 0 || K <= 0) return QV_ERR_SHAPE;
   if ((K % k_step) != 0 || K > 65536 || (N % 128) != 0) return QV_ERR_UNSUPPORTED;
   if (ldy < N) return QV_ERR_SHAPE;
+  // output rows below 16 MiB: the epilogue addresses a tile's rows with 32-bit offsets
+  if (ldy * dtype_bytes(yt) >= (int64_t{1} << 24)) return QV_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return QV_OK;
   if (!Xq || !xs || !Wq || !ws || !Y) return QV_ERR_NULL;
   if (!aligned(Xq) || !aligned(Wq) || !aligned(ws) || !aligned(bias) || !aligned(Y) ||

@@ -499,6 +499,29 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
   constexpr int kChunksPerRow = WN * (int)sizeof(OutT) / 16;  // 16-byte chunks per row
   constexpr int kRowsPerPass = 64 / kChunksPerRow;            // rows one wave-wide read covers
 
+  // Output stores.  The wave's block of rows m0 + wm*WM + (0..WM-1) is written through a buffer
+  // resource that starts at the block's first output and ends after its last row below M: a store
+  // to a row at or past M falls outside the range and is dropped, so the lanes need no bounds test
+  // and no 64-bit address; the row offset of a pass is a scalar operand.  The host admits output
+  // rows below 2^24 bytes, so the block's WM <= 128 rows span less than 2^31 bytes.
+  static_assert(WM <= 128, "32-bit output offsets");
+  const int64_t row_stride = ldy * (int64_t)sizeof(OutT);
+  const int64_t rows_left = M - (m0 + wm * WM);
+  const int rows = rows_left < 0 ? 0 : (rows_left > WM ? WM : (int)rows_left);
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t yrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<OutT*>(Y) + (m0 + wm * WM) * ldy + n0 + wn * WN, (short)0, (int)(rows * row_stride), kBufDword3);
+  const uint32_t lane_off = (uint32_t)((lane / kChunksPerRow) * row_stride) + 16u * (uint32_t)(lane % kChunksPerRow);
+#endif
+  // Row ru + lane / kChunksPerRow of the block (ru uniform), chunk lane % kChunksPerRow.
+  auto store_out = [&](int ru, const u32x4& v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_buffer_store_b128(v, yrsrc, lane_off, (uint32_t)(ru * row_stride), 2 /* nt */);
+#else
+    (void)ru; (void)v; (void)rows;  // the host pass compiles no kernel code
+#endif
+  };
+
   // bf16 outputs are staged without a block barrier: after the last stage's barrier no wave reads
   // any ring buffer but the last stage's (every LDS-DMA has landed, no refill follows), so buffer
   // nk % STAGES is free.  Each wave stages its block in 32-row passes (one fragment row c at a
@@ -530,12 +553,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
       for (int pass = 0; pass < 32 / kRowsPerPass; ++pass) {
         const int ml = pass * kRowsPerPass + lane / kChunksPerRow;
         const int ch = lane % kChunksPerRow;
-        const int64_t m = m0 + wm * WM + 32 * c + ml;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stage_out + ml * 128 + 16 * (ch ^ (ml & 7)));
-        if (m < M) {
-          uint8_t* out = reinterpret_cast<uint8_t*>(static_cast<OutT*>(Y) + m * ldy + n0 + wn * WN) + 16 * ch;
-          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out));
-        }
+        store_out(32 * c + pass * kRowsPerPass, v);
       }
       // the next pass rewrites this slice after the reads above
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -574,12 +593,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
     for (int pass = 0; pass < WM / kRowsPerPass; ++pass) {
       const int ml = pass * kRowsPerPass + lane / kChunksPerRow;
       const int ch = lane % kChunksPerRow;
-      const int64_t m = m0 + wm * WM + ml;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage_out + ml * kOutRowBytes + 16 * ch);
-      if (m < M) {
-        uint8_t* out = reinterpret_cast<uint8_t*>(static_cast<OutT*>(Y) + m * ldy + n0 + wn * WN) + 16 * ch;
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out));
-      }
+      store_out(pass * kRowsPerPass, v);
     }
   }
 }

@@ -99,7 +99,8 @@ qv_status qv_pack_weights(const void* W, qv_dtype w_dtype, int64_t N, int64_t K,
  *   bias [N] fp32 or NULL.
  *   K  multiple of 128 in [128, 65536] (the accumulator stays exact);  N multiple of 128;  M >= 0.
  *   epi QV_EPI_NONE or QV_EPI_GELU (GELU(y) = 0.5 y erfc(-y / sqrt 2), applied after the bias).
- *   Y  [M][ldy] fp32 or bf16 (y_dtype, bf16 rounded to nearest even), ldy >= N.
+ *   Y  [M][ldy] fp32 or bf16 (y_dtype, bf16 rounded to nearest even), ldy >= N, and a row of
+ *      ldy outputs below 2^24 bytes (else QV_ERR_UNSUPPORTED).
  */
 qv_status qv_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq, const float* w_scale,
                        const float* bias, int64_t M, int64_t N, int64_t K, qv_epilogue epi, void* Y,

@@ -103,6 +103,12 @@ def test_gemm_argument_errors(L):
     assert gemm(L, bias=P_MIS) == QV_ERR_ALIGN
     assert gemm(L, Wq=P_MIS) == QV_ERR_ALIGN
     assert gemm(L, yt=1, ldy=132) == QV_ERR_ALIGN     # bf16 row stride of 264 bytes
+    # output rows of 2^24 bytes or more are outside the epilogue's 32-bit tile offsets
+    # (M = 0: the shape checks run, nothing is launched)
+    assert gemm(L, M=0, yt=0, ldy=1 << 22) == QV_ERR_UNSUPPORTED
+    assert gemm(L, M=0, yt=1, ldy=1 << 23) == QV_ERR_UNSUPPORTED
+    assert gemm(L, M=0, yt=0, ldy=(1 << 22) - 4) == QV_OK
+    assert gemm(L, M=0, yt=1, ldy=(1 << 23) - 8) == QV_OK
 
 
 def test_linear_argument_errors(L):
