@@ -33,6 +33,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #ifndef QV_RQ_WAVES
 #define QV_RQ_WAVES 5
 #endif
+#ifndef QV_RQM_WAVES
+#define QV_RQM_WAVES 3  // waves per SIMD of the matrix-core kernel (132 registers with the prefetch)
+#endif
+#ifndef QV_RQ_MFMA
+#define QV_RQ_MFMA 1  // 1: bf16 rows of width 4096 with one scale per row use the matrix-core kernel
+#endif
+#ifndef QV_RQ_MFMA_1024
+// 1: width 1024 too.  On the 32-frame block (43968 rows) it measured level with or ~1.5 us slower
+// than the butterfly kernel; at 4x the rows it streams 17 % faster.
+#define QV_RQ_MFMA_1024 0
+#endif
 #ifndef QV_RQ_PREFETCH
 #define QV_RQ_PREFETCH 0  // 1: keep the next row group's raw data in registers (3 waves/SIMD instead of 4)
 #endif
@@ -281,6 +292,205 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(K == 4
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// bf16 rows with one scale per row: the first five index bits on the matrix cores.
+//
+// With k = 32 a + b, the Sylvester-order H_K is H_{K/32} (x) H_32, so the rotation is the 32-point
+// transform over b followed by the (K/32)-point transform over a.  bf16 inputs and the +-1 entries
+// of H_32 are exact MFMA operands, so v_mfma_f32_16x16x32_bf16 forms the b-transform with fp32
+// accumulation and no unpacking: the loaded data is the B operand (k = b, column n = one of 16
+// a-values held by the 16 lanes of a DPP row), a constant slice of H_32 the A operand (16 of the 32
+// output indices b'), and two MFMAs (q = 0, 1) give all 32 b'.  Output row m = 4 (l / 16) + r of
+// MFMA q is assigned b' = r + 4 q + 8 (l / 16), so a lane ends with the 8 consecutive channels
+// b' = 8 (l / 16) + e, e = 4 q + r: one packed dword.  The a-transform remains: the low bits of a sit
+// on lane bits (DPP butterflies, as in fwht_regs.h), the tile index J (3 bits) in registers.
+//   K = 1024: DPP-row position p = 4 t + a_lo holds row t of the wave's 4 and a_lo = p & 3;
+//             a = 4 J + a_lo (2 DPP stages, 3 in-lane stages);
+//   K = 4096: one row per wave, p holds a_lo = chunk_of_lane16(p); a = 16 J + a_lo (4 DPP stages,
+//             3 in-lane stages).
+// Every element of the MFMA sum is an exact product and the fp32 accumulation of the 32 terms
+// stays within the rounding error of the five butterfly stages it replaces.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+template <int K>
+struct MfmaLayout {
+  static constexpr int kRowsPerWave = (K == 1024) ? 4 : 1;
+  static constexpr int kLanesA = (K == 1024) ? 4 : 16;  // a-values per DPP row and row
+  static constexpr int kTableRows = (K == 1024) ? 16 : 64;
+  static constexpr float kNorm = (K == 1024) ? 0.03125f : 0.015625f;  // 1/sqrt(K), exact
+};
+
+// a_lo held by DPP-row position p; the DPP butterflies leave the sign (-1)^popcount(a_lo) on its
+// elements, which the factor table folds in.
+template <int K>
+__device__ __forceinline__ int mfma_alo(int p) {
+  return (K == 1024) ? (p & 3) : chunk_of_lane16(p);
+}
+
+// Factor table: row (l / 16) * kLanesA + a_lo-position holds, for J = 0..7 and e = 0..7, the factor
+// sign * 1/sqrt(K) * mult[k'] of channel k' = 8 (l / 16) + e + 32 (kLanesA J + a_lo).
+template <int K>
+__device__ __forceinline__ int mfma_table_row(int lane) {
+  return (K == 1024) ? ((lane >> 4) * 4 + (lane & 3)) : lane;
+}
+
+template <int K>
+__device__ __forceinline__ void fill_mfma_table(const float* __restrict__ mult, float* cm) {
+  using L = MfmaLayout<K>;
+  for (int idx = threadIdx.x; idx < L::kTableRows * 64; idx += kThreads) {
+    const int row = idx >> 6, je = idx & 63, J = je >> 3, e = je & 7;
+    const int g = (K == 1024) ? (row >> 2) : (row >> 4);
+    const int alo = (K == 1024) ? (row & 3) : chunk_of_lane16(row & 15);
+    const int k = 8 * g + e + 32 * (L::kLanesA * J + alo);
+    const float sign = (__builtin_popcount(alo) & 1) ? -1.0f : 1.0f;
+    cm[row * kCmStride + je] = sign * L::kNorm * (mult ? mult[k] : 1.0f);
+  }
+}
+
+template <int K, int kBits>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QV_RQM_WAVES))) void rotate_quant_mfma_kernel(
+    const uint16_t* __restrict__ X, int64_t M, int64_t ldx, const float* __restrict__ mult,
+    uint8_t* __restrict__ Xq, float* __restrict__ x_scale) {
+  using L = MfmaLayout<K>;
+  __shared__ __attribute__((aligned(16))) float cm_lds[L::kTableRows * kCmStride];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p = lane & 15, g = lane >> 4;
+  const int t = (K == 1024) ? (p >> 2) : 0;  // row of the lane inside the wave's group
+  const int alo = mfma_alo<K>(p);
+  const float* cm_row = cm_lds + mfma_table_row<K>(lane) * kCmStride;
+
+  // A operands: lane l holds row m = l % 16 and k = 8 (l / 16) + j of the 16 x 32 slice; row m of
+  // slice q is output b' = (m % 4) + 4 q + 8 (m / 4), so entry j is (-1)^popcount(b' & (8 g + j)).
+  bf16x8 hq[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int bp = (p & 3) + 4 * q + 8 * (p >> 2);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = (__builtin_popcount(bp & (8 * g + 2 * i)) & 1) ? 0xBF80u : 0x3F80u;
+      const uint32_t hi = (__builtin_popcount(bp & (8 * g + 2 * i + 1)) & 1) ? 0xBF80u : 0x3F80u;
+      w[i] = lo | (hi << 16);
+    }
+    hq[q] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
+  }
+  // DPP butterfly signs: +1 on the lower element of a pair, -1 on the upper.
+  float sigma[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) sigma[s] = ((alo >> s) & 1) ? -1.0f : 1.0f;
+
+  const int64_t groups = (M + L::kRowsPerWave - 1) / L::kRowsPerWave;
+  const int64_t wave_stride = (int64_t)gridDim.x * (kThreads / 64);
+  int64_t grp = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+
+  // Lane's 16-byte share of tile J: elements 32 (kLanesA J + a_lo) + 8 g + 0..7 of its row.
+  // Rows past the end are clamped to the last row: loaded and transformed, never stored.
+  const uint32_t lane_off = (uint32_t)(32 * alo + 8 * g);
+  auto load_tiles = [&](int64_t gr, u32x4 (&raw)[8]) {
+    const int64_t r0 = gr * L::kRowsPerWave, row = r0 + t;
+    const uint16_t* xrow = X + r0 * ldx + (uint32_t)(((row < M ? row : M - 1) - r0) * ldx) + lane_off;
+#pragma unroll
+    for (int J = 0; J < 8; ++J)
+      raw[J] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + 32 * L::kLanesA * J));
+  };
+  // The first row group is requested before the factor table is built, and each next one as soon
+  // as the matrix cores have read the current tiles, so its loads are in flight during the
+  // butterflies, the quantization and the stores.
+  u32x4 raw[8];
+  if (grp < groups) load_tiles(grp, raw);
+  fill_mfma_table<K>(mult, cm_lds);
+  __syncthreads();
+
+  for (; grp < groups; grp += wave_stride) {
+    const int64_t r0 = grp * L::kRowsPerWave;
+    const int64_t row = r0 + t;
+    float v[8][8];
+#pragma unroll
+    for (int J = 0; J < 8; ++J) {
+      const bf16x8 b = __builtin_bit_cast(bf16x8, raw[J]);
+      const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hq[0], b, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      const f32x4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hq[1], b, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // copy each element to a scalar first: a bit-cast of a vector element reads element 0
+        const float x0 = d0[r], x1 = d1[r];
+        v[J][r] = x0;
+        v[J][4 + r] = x1;
+      }
+    }
+    if (grp + wave_stride < groups) load_tiles(grp + wave_stride, raw);
+
+    // a-transform: low bits across the DPP row, then the tile bits in-lane.
+    float* vr = &v[0][0];
+    dpp_stage<0>(vr, sigma[0]);
+    dpp_stage<1>(vr, sigma[1]);
+    if constexpr (K == 4096) {
+      dpp_stage<2>(vr, sigma[2]);
+      dpp_stage<3>(vr, sigma[3]);
+    }
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+      for (int J = 0; J < 8; ++J) {
+        if ((J & h) == 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float a = v[J][e], b = v[J + h][e];
+            v[J][e] = a + b;
+            v[J + h][e] = a - b;
+          }
+        }
+      }
+    }
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int J = 0; J < 8; ++J) {
+      const float4 c0 = *reinterpret_cast<const float4*>(cm_row + 8 * J);
+      const float4 c1 = *reinterpret_cast<const float4*>(cm_row + 8 * J + 4);
+      const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[J][e] *= c[e];
+        amax = fmaxf(amax, fabsf(v[J][e]));
+      }
+    }
+    // Row maximum: over the a_lo lanes of the row (quad for K = 1024, DPP row for 4096) and the
+    // four DPP rows (b' groups).
+    amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0xB1, 0xF, 0xF, true)));
+    amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0x4E, 0xF, 0xF, true)));
+    if constexpr (K == 4096) {
+      amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0x128, 0xF, 0xF, true)));
+      amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0x140, 0xF, 0xF, true)));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    constexpr float kQmax = (float)((1 << (kBits - 1)) - 1);
+    float s = amax / kQmax;
+    if (!(s >= 1.17549435e-38f)) s = 0.0f;  // zero or subnormal scale: all-zero row
+    const float rs = (s > 0.0f) ? 1.0f / s : 0.0f;
+
+    if (row < M) {
+      uint8_t* const qrow = Xq + r0 * (K * kBits / 8) + (uint32_t)(t * (K * kBits / 8));
+#pragma unroll
+      for (int J = 0; J < 8; ++J) {
+        uint32_t m[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m[e] = __builtin_bit_cast(uint32_t, __builtin_fmaf(v[J][e], rs, kMagic<kBits>));
+        // channels 8 g + 32 a + 0..7, a = kLanesA J + a_lo
+        const int idx = g + 4 * (L::kLanesA * J + alo);
+        if constexpr (kBits == 4) {
+          reinterpret_cast<uint32_t*>(qrow)[idx] = pack8(m);
+        } else {
+          reinterpret_cast<uint2*>(qrow)[idx] = pack8_int8(m);
+        }
+      }
+      if ((lane & (K == 1024 ? 0x33 : 0x3F)) == 0) x_scale[row] = s;
+    }
+  }
+}
+
 // Column-wise maximum of |rotated value| over rows (calibration statistics).  Each lane keeps the
 // running maxima of the 64 channels it owns; non-negative floats order like their bit patterns,
 // so the cross-block combine is an integer atomic max (order-independent, deterministic).
@@ -372,6 +582,15 @@ hipError_t launch_rq(const void* X, int64_t M, int64_t ld, const float* mult, ui
   return hipGetLastError();
 }
 
+template <int K, int kBits>
+hipError_t launch_rq_mfma(const void* X, int64_t M, int64_t ld, const float* mult, uint8_t* q, float* scale,
+                          hipStream_t st) {
+  const int grid = grid_for_rows(M, MfmaLayout<K>::kRowsPerWave, resident_grid<rotate_quant_mfma_kernel<K, kBits>>());
+  hipLaunchKernelGGL((rotate_quant_mfma_kernel<K, kBits>), dim3(grid), dim3(kThreads), 0, st,
+                     static_cast<const uint16_t*>(X), M, ld, mult, q, scale);
+  return hipGetLastError();
+}
+
 template <int K, int kGroup>
 hipError_t launch_rq_grouped(const void* X, bool bf16, int64_t M, int64_t ld, const float* mult, uint8_t* q,
                              float* scale, hipStream_t st) {
@@ -391,6 +610,16 @@ hipError_t launch_colmax(const void* X, int64_t M, int64_t ld, unsigned* colmax,
 
 hipError_t launch_rotate_quant(const void* X, bool bf16, int64_t M, int64_t K, int64_t ld, const float* mult,
                                uint8_t* q, float* scale, int bits, hipStream_t st) {
+  if constexpr (QV_RQ_MFMA) {
+    if (bf16 && K == 4096)
+      return bits == 8 ? launch_rq_mfma<4096, 8>(X, M, ld, mult, q, scale, st)
+                       : launch_rq_mfma<4096, 4>(X, M, ld, mult, q, scale, st);
+  }
+  if constexpr (QV_RQ_MFMA_1024) {
+    if (bf16 && K == 1024)
+      return bits == 8 ? launch_rq_mfma<1024, 8>(X, M, ld, mult, q, scale, st)
+                       : launch_rq_mfma<1024, 4>(X, M, ld, mult, q, scale, st);
+  }
   if (bits == 8) {
     if (K == 1024) {
       return bf16 ? launch_rq<1024, uint16_t, 8>(X, M, ld, mult, q, scale, st)

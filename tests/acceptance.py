@@ -5,7 +5,10 @@ value; the kernel sums the butterflies in fp32 and multiplies by the reciprocal 
 two can disagree only where x / s lies within the kernel's rounding error of a half-integer.  For
 every element this module bounds that error (first order, with a factor 2 of margin):
   * butterflies: each of the log2(K) stages rounds once, and the rounding errors feeding one output
-    sum to at most log2(K) * u * sum_i |x_i| before the 1/sqrt(K) scaling (u = 2^-24);
+    sum to at most log2(K) * u * sum_i |x_i| before the 1/sqrt(K) scaling (u = 2^-24).  Where the
+    kernel forms the first five stages as one fp32 matrix-core sum of 32 exact products (bf16 rows
+    of width 4096), that sum's error is measured below 3 u * sum |x| over its 32 terms, inside the
+    5 u the five stages are allowed;
   * the smoothing product, the reciprocal of the scale and the fused rounding add a few u * |t|;
   * the row maximum, hence the scale, moves by at most the butterfly bound of its element.
 A GPU code is admissible when it lies between rne(t - tau) and rne(t + tau), t the exact code-space
