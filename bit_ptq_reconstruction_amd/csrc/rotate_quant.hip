@@ -11,9 +11,13 @@
 // x * fl(1/s) rounded once to an integer (a fused multiply-add onto 1.5 * 2^23 + 8).  That differs
 // from a correctly rounded quotient only when x / s lies within a few ulp of a half-integer.
 //
-// Work split: K = 1024 puts one row on 16 lanes (4 rows per wave), K = 4096 one row per wave;
-// every lane holds 64 values (fwht_regs.h).  Loads are 16-byte per lane and each 16-lane row
-// group covers 256 contiguous bytes; every lane writes one packed dword per 8 elements.
+// Two kernels.  The butterfly kernel (rotate_quant_kernel) runs every log2(K) stage on the vector
+// ALU: K = 1024 puts one row on 16 lanes (4 rows per wave), K = 4096 one row per wave, and every
+// lane holds 64 values (fwht_regs.h).  The matrix-core kernel (rotate_quant_mfma_kernel), used for
+// bf16 rows of width 4096 with one scale per row, forms the first five stages as an exact-operand
+// bf16 MFMA product with H_32 and the rest as butterflies (see its comment).  In both, loads are
+// 16-byte per lane over contiguous 256-byte or larger runs, and every lane writes one packed dword
+// per 8 elements.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 #include <stdint.h>
