@@ -15,6 +15,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -50,10 +51,15 @@ def parse_args():
 
 
 def kernel_source_hash(names):
+    """Hash of the kernel sources' code: comments and whitespace are dropped first, so that a
+    counter summary stays matched to its kernels until their code changes."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "bit_ptq_reconstruction_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "bit_ptq_reconstruction_amd", "csrc", n), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
