@@ -44,8 +44,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define QV_RQ_MFMA 1  // 1: bf16 rows of width 4096 with one scale per row use the matrix-core kernel
 #endif
 #ifndef QV_RQ_MFMA_1024
-// 1: width 1024 too.  On the 32-frame block (43968 rows) it measured level with or ~1.5 us slower
-// than the butterfly kernel; at 4x the rows it streams 17 % faster.
+// 1: width 1024 too.  Timed back to back it measured level with the butterfly kernel (26 vs 25 us
+// at 43968 rows, 86 vs 85 us at four times that), so the butterfly kernel keeps that width.
 #define QV_RQ_MFMA_1024 0
 #endif
 #ifndef QV_RQ_PREFETCH
