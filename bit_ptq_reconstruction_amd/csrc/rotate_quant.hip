@@ -43,10 +43,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #ifndef QV_RQ_MFMA
 #define QV_RQ_MFMA 1  // 1: bf16 rows of width 4096 with one scale per row use the matrix-core kernel
 #endif
+#ifndef QV_RQM_LANES_1024
+// a-values per DPP row of the width-1024 matrix-core kernel: 8 (2 rows per wave, 32 values per
+// lane, 96 registers, 5 waves) measured 5 % faster than the butterfly kernel; 4 (4 rows per wave,
+// 64 values, 151 registers, 3 waves) measured level with it.
+#define QV_RQM_LANES_1024 8
+#endif
+#ifndef QV_RQM_WAVES_1024
+#define QV_RQM_WAVES_1024 (QV_RQM_LANES_1024 == 8 ? 5 : 3)
+#endif
 #ifndef QV_RQ_MFMA_1024
-// 1: width 1024 too.  Timed back to back it measured level with the butterfly kernel (26 vs 25 us
-// at 43968 rows, 86 vs 85 us at four times that), so the butterfly kernel keeps that width.
-#define QV_RQ_MFMA_1024 0
+#define QV_RQ_MFMA_1024 1  // 1: bf16 rows of width 1024 with one scale per row use the matrix-core kernel
 #endif
 #ifndef QV_RQ_PREFETCH
 #define QV_RQ_PREFETCH 0  // 1: keep the next row group's raw data in registers (3 waves/SIMD instead of 4)
@@ -316,53 +323,78 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(K == 4
 // stays within the rounding error of the five butterfly stages it replaces.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-template <int K>
+// LA a-values per row on the 16 lanes of a DPP row (4, 8 or 16), so 16 / LA rows per wave and
+// K / (32 LA) tiles J per row in registers.
+template <int K, int LA>
 struct MfmaLayout {
-  static constexpr int kRowsPerWave = (K == 1024) ? 4 : 1;
-  static constexpr int kLanesA = (K == 1024) ? 4 : 16;  // a-values per DPP row and row
-  static constexpr int kTableRows = (K == 1024) ? 16 : 64;
+  static_assert(LA == 4 || LA == 8 || LA == 16, "a-values per DPP row");
+  static constexpr int kRowsPerWave = 16 / LA;
+  static constexpr int kTiles = K / (32 * LA);
+  static constexpr int kValues = 8 * kTiles;  // per lane and row
+  static constexpr int kTableRows = 4 * LA;
+  static constexpr int kDppStages = LA == 4 ? 2 : (LA == 8 ? 3 : 4);
   static constexpr float kNorm = (K == 1024) ? 0.03125f : 0.015625f;  // 1/sqrt(K), exact
+  static_assert(kTiles * 32 * LA == K && kValues <= 64, "layout");
 };
 
-// a_lo held by DPP-row position p; the DPP butterflies leave the sign (-1)^popcount(a_lo) on its
-// elements, which the factor table folds in.
-template <int K>
-__device__ __forceinline__ int mfma_alo(int p) {
-  return (K == 1024) ? (p & 3) : chunk_of_lane16(p);
+// a_lo held by position pp = p % LA of a row's lanes.  The map is chosen so that the butterfly
+// partner along a_lo bit s is lane pp ^ {1, 2, 7 or 8, 15}[s]: quad_perm for bits 0 and 1,
+// row_half_mirror (LA = 8) or row_ror:8 (LA = 16) for bit 2, row_mirror for bit 3.  The DPP
+// butterflies leave the sign (-1)^popcount(a_lo) on a lane's elements; the factor table folds it in.
+template <int LA>
+__device__ __forceinline__ int mfma_alo(int pp) {
+  if constexpr (LA == 4) return pp;
+  if constexpr (LA == 8) return ((pp ^ (pp >> 2)) & 1) | ((((pp >> 1) ^ (pp >> 2)) & 1) << 1) | (pp & 4);
+  return chunk_of_lane16(pp);
 }
 
-// Factor table: row (l / 16) * kLanesA + a_lo-position holds, for J = 0..7 and e = 0..7, the factor
-// sign * 1/sqrt(K) * mult[k'] of channel k' = 8 (l / 16) + e + 32 (kLanesA J + a_lo).
-template <int K>
-__device__ __forceinline__ int mfma_table_row(int lane) {
-  return (K == 1024) ? ((lane >> 4) * 4 + (lane & 3)) : lane;
+// One DPP butterfly stage over N registers: self + sigma * partner (see fwht_regs.h).
+template <int LA, int S, int N>
+__device__ __forceinline__ void mfma_dpp_stage(float* r, float sigma) {
+#pragma unroll
+  for (int i = 0; i < N; i += 16) {
+    if constexpr (S == 0) QV_DPP16("quad_perm:[1,0,3,2]", (r + i), sigma);
+    if constexpr (S == 1) QV_DPP16("quad_perm:[2,3,0,1]", (r + i), sigma);
+    if constexpr (S == 2 && LA == 8) QV_DPP16("row_half_mirror", (r + i), sigma);
+    if constexpr (S == 2 && LA == 16) QV_DPP16("row_ror:8", (r + i), sigma);
+    if constexpr (S == 3) QV_DPP16("row_mirror", (r + i), sigma);
+  }
 }
 
-template <int K>
+// Factor table: row g LA + pp holds, for J < kTiles and e < 8, the factor
+// sign * 1/sqrt(K) * mult[k'] of channel k' = 8 g + e + 32 (LA J + a_lo(pp)).
+template <int K, int LA>
 __device__ __forceinline__ void fill_mfma_table(const float* __restrict__ mult, float* cm) {
-  using L = MfmaLayout<K>;
-  for (int idx = threadIdx.x; idx < L::kTableRows * 64; idx += kThreads) {
-    const int row = idx >> 6, je = idx & 63, J = je >> 3, e = je & 7;
-    const int g = (K == 1024) ? (row >> 2) : (row >> 4);
-    const int alo = (K == 1024) ? (row & 3) : chunk_of_lane16(row & 15);
-    const int k = 8 * g + e + 32 * (L::kLanesA * J + alo);
+  using L = MfmaLayout<K, LA>;
+  for (int idx = threadIdx.x; idx < L::kTableRows * L::kValues; idx += kThreads) {
+    const int row = idx / L::kValues, je = idx % L::kValues, J = je >> 3, e = je & 7;
+    const int g = row / LA, alo = mfma_alo<LA>(row % LA);
+    const int k = 8 * g + e + 32 * (LA * J + alo);
     const float sign = (__builtin_popcount(alo) & 1) ? -1.0f : 1.0f;
     cm[row * kCmStride + je] = sign * L::kNorm * (mult ? mult[k] : 1.0f);
   }
 }
 
-template <int K, int kBits>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QV_RQM_WAVES))) void rotate_quant_mfma_kernel(
+// Waves per SIMD the register allocation must allow.  The 8-bit width-1024 instance needs a few
+// more registers (two dwords of codes per 8 channels) and would spill at 5.
+template <int K, int kBits, int LA>
+constexpr int mfma_waves() {
+  return K == 1024 ? (kBits == 8 && QV_RQM_WAVES_1024 > 4 ? 4 : QV_RQM_WAVES_1024) : QV_RQM_WAVES;
+}
+
+template <int K, int kBits, int LA>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mfma_waves<K, kBits, LA>()))) void rotate_quant_mfma_kernel(
     const uint16_t* __restrict__ X, int64_t M, int64_t ldx, const float* __restrict__ mult,
     uint8_t* __restrict__ Xq, float* __restrict__ x_scale) {
-  using L = MfmaLayout<K>;
+  using L = MfmaLayout<K, LA>;
+  constexpr int T = L::kTiles;
   __shared__ __attribute__((aligned(16))) float cm_lds[L::kTableRows * kCmStride];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = lane & 15, g = lane >> 4;
-  const int t = (K == 1024) ? (p >> 2) : 0;  // row of the lane inside the wave's group
-  const int alo = mfma_alo<K>(p);
-  const float* cm_row = cm_lds + mfma_table_row<K>(lane) * kCmStride;
+  const int t = p / LA;  // row of the lane inside the wave's group
+  const int alo = mfma_alo<LA>(p % LA);
+  const float* cm_row = cm_lds + (g * LA + p % LA) * kCmStride;
 
   // A operands: lane l holds row m = l % 16 and k = 8 (l / 16) + j of the 16 x 32 slice; row m of
   // slice q is output b' = (m % 4) + 4 q + 8 (m / 4), so entry j is (-1)^popcount(b' & (8 g + j)).
@@ -388,30 +420,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QV_RQM
   const int64_t wave_stride = (int64_t)gridDim.x * (kThreads / 64);
   int64_t grp = (int64_t)blockIdx.x * (kThreads / 64) + wave;
 
-  // Lane's 16-byte share of tile J: elements 32 (kLanesA J + a_lo) + 8 g + 0..7 of its row.
+  // Lane's 16-byte share of tile J: elements 32 (LA J + a_lo) + 8 g + 0..7 of its row.
   // Rows past the end are clamped to the last row: loaded and transformed, never stored.
   const uint32_t lane_off = (uint32_t)(32 * alo + 8 * g);
-  auto load_tiles = [&](int64_t gr, u32x4 (&raw)[8]) {
+  auto load_tiles = [&](int64_t gr, u32x4 (&raw)[T]) {
     const int64_t r0 = gr * L::kRowsPerWave, row = r0 + t;
     const uint16_t* xrow = X + r0 * ldx + (uint32_t)(((row < M ? row : M - 1) - r0) * ldx) + lane_off;
 #pragma unroll
-    for (int J = 0; J < 8; ++J)
-      raw[J] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + 32 * L::kLanesA * J));
+    for (int J = 0; J < T; ++J)
+      raw[J] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + 32 * LA * J));
   };
   // The first row group is requested before the factor table is built, and each next one as soon
   // as the matrix cores have read the current tiles, so its loads are in flight during the
   // butterflies, the quantization and the stores.
-  u32x4 raw[8];
+  u32x4 raw[T];
   if (grp < groups) load_tiles(grp, raw);
-  fill_mfma_table<K>(mult, cm_lds);
+  fill_mfma_table<K, LA>(mult, cm_lds);
   __syncthreads();
 
   for (; grp < groups; grp += wave_stride) {
     const int64_t r0 = grp * L::kRowsPerWave;
     const int64_t row = r0 + t;
-    float v[8][8];
+    float v[T][8];
 #pragma unroll
-    for (int J = 0; J < 8; ++J) {
+    for (int J = 0; J < T; ++J) {
       const bf16x8 b = __builtin_bit_cast(bf16x8, raw[J]);
       const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hq[0], b, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       const f32x4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hq[1], b, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -427,16 +459,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QV_RQM
 
     // a-transform: low bits across the DPP row, then the tile bits in-lane.
     float* vr = &v[0][0];
-    dpp_stage<0>(vr, sigma[0]);
-    dpp_stage<1>(vr, sigma[1]);
-    if constexpr (K == 4096) {
-      dpp_stage<2>(vr, sigma[2]);
-      dpp_stage<3>(vr, sigma[3]);
-    }
+    mfma_dpp_stage<LA, 0, 8 * T>(vr, sigma[0]);
+    mfma_dpp_stage<LA, 1, 8 * T>(vr, sigma[1]);
+    if constexpr (L::kDppStages > 2) mfma_dpp_stage<LA, 2, 8 * T>(vr, sigma[2]);
+    if constexpr (L::kDppStages > 3) mfma_dpp_stage<LA, 3, 8 * T>(vr, sigma[3]);
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
+    for (int h = 1; h < T; h <<= 1) {
 #pragma unroll
-      for (int J = 0; J < 8; ++J) {
+      for (int J = 0; J < T; ++J) {
         if ((J & h) == 0) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -450,7 +480,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QV_RQM
 
     float amax = 0.0f;
 #pragma unroll
-    for (int J = 0; J < 8; ++J) {
+    for (int J = 0; J < T; ++J) {
       const float4 c0 = *reinterpret_cast<const float4*>(cm_row + 8 * J);
       const float4 c1 = *reinterpret_cast<const float4*>(cm_row + 8 * J + 4);
       const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
@@ -460,11 +490,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QV_RQM
         amax = fmaxf(amax, fabsf(v[J][e]));
       }
     }
-    // Row maximum: over the a_lo lanes of the row (quad for K = 1024, DPP row for 4096) and the
-    // four DPP rows (b' groups).
+    // Row maximum: over the row's LA lanes of each DPP row, then over the four DPP rows.
     amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0xB1, 0xF, 0xF, true)));
     amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0x4E, 0xF, 0xF, true)));
-    if constexpr (K == 4096) {
+    if constexpr (LA == 8) {
+      amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0x141, 0xF, 0xF, true)));
+    } else if constexpr (LA == 16) {
       amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0x128, 0xF, 0xF, true)));
       amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0x140, 0xF, 0xF, true)));
     }
@@ -478,19 +509,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QV_RQM
     if (row < M) {
       uint8_t* const qrow = Xq + r0 * (K * kBits / 8) + (uint32_t)(t * (K * kBits / 8));
 #pragma unroll
-      for (int J = 0; J < 8; ++J) {
+      for (int J = 0; J < T; ++J) {
         uint32_t m[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) m[e] = __builtin_bit_cast(uint32_t, __builtin_fmaf(v[J][e], rs, kMagic<kBits>));
-        // channels 8 g + 32 a + 0..7, a = kLanesA J + a_lo
-        const int idx = g + 4 * (L::kLanesA * J + alo);
+        // channels 8 g + 32 a + 0..7, a = LA J + a_lo
+        const int idx = g + 4 * (LA * J + alo);
         if constexpr (kBits == 4) {
           reinterpret_cast<uint32_t*>(qrow)[idx] = pack8(m);
         } else {
           reinterpret_cast<uint2*>(qrow)[idx] = pack8_int8(m);
         }
       }
-      if ((lane & (K == 1024 ? 0x33 : 0x3F)) == 0) x_scale[row] = s;
+      if ((lane & (0x30 | (LA - 1))) == 0) x_scale[row] = s;
     }
   }
 }
@@ -589,8 +620,10 @@ hipError_t launch_rq(const void* X, int64_t M, int64_t ld, const float* mult, ui
 template <int K, int kBits>
 hipError_t launch_rq_mfma(const void* X, int64_t M, int64_t ld, const float* mult, uint8_t* q, float* scale,
                           hipStream_t st) {
-  const int grid = grid_for_rows(M, MfmaLayout<K>::kRowsPerWave, resident_grid<rotate_quant_mfma_kernel<K, kBits>>());
-  hipLaunchKernelGGL((rotate_quant_mfma_kernel<K, kBits>), dim3(grid), dim3(kThreads), 0, st,
+  constexpr int LA = K == 1024 ? QV_RQM_LANES_1024 : 16;
+  const int grid = grid_for_rows(M, MfmaLayout<K, LA>::kRowsPerWave,
+                                 resident_grid<rotate_quant_mfma_kernel<K, kBits, LA>>());
+  hipLaunchKernelGGL((rotate_quant_mfma_kernel<K, kBits, LA>), dim3(grid), dim3(kThreads), 0, st,
                      static_cast<const uint16_t*>(X), M, ld, mult, q, scale);
   return hipGetLastError();
 }

@@ -75,9 +75,10 @@ def check_quant_against_oracle(X, mult, q_packed, s_gpu, mode, label):
     (1024, "fp32", 1, True, 0), (1024, "fp32", 5, False, 0), (1024, "bf16", 1374, True, 0),
     (1024, "fp32", 1375, True, 64), (4096, "bf16", 1, True, 0), (4096, "bf16", 137, True, 0),
     (4096, "fp32", 70, False, 32), (1024, "bf16", 257, True, 8),
-    # bf16 rows of width 4096 take the matrix-core kernel: padded rows, and enough rows that every
-    # wave transforms several groups with the next group's loads in flight
-    (4096, "bf16", 7001, True, 8),
+    # bf16 rows take the matrix-core kernel: padded rows, an odd row count (the last group of a
+    # 2-row wave is half empty at width 1024), and enough rows that every wave transforms several
+    # groups with the next group's loads in flight
+    (4096, "bf16", 7001, True, 8), (1024, "bf16", 20001, True, 8),
 ])
 def test_hadamard_smooth_quant_parity(qv, dev, K, dtype, M, smooth, pad):
     X = synth.vggt_activations(M, K, seed=K + M, dtype=dtype)
