@@ -38,7 +38,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define QV_RQ_WAVES 5
 #endif
 #ifndef QV_RQM_WAVES
-#define QV_RQM_WAVES 3  // waves per SIMD of the matrix-core kernel (132 registers with the prefetch)
+#define QV_RQM_WAVES 3  // waves per SIMD of the width-4096 matrix-core kernel (134 registers with the prefetch)
 #endif
 #ifndef QV_RQ_MFMA
 #define QV_RQ_MFMA 1  // 1: bf16 rows of width 4096 with one scale per row use the matrix-core kernel
