@@ -78,7 +78,7 @@ def check_quant_against_oracle(X, mult, q_packed, s_gpu, mode, label):
     # bf16 rows take the matrix-core kernel: padded rows, an odd row count (the last group of a
     # 2-row wave is half empty at width 1024), and enough rows that every wave transforms several
     # groups with the next group's loads in flight
-    (4096, "bf16", 7001, True, 8), (1024, "bf16", 20001, True, 8),
+    (4096, "bf16", 7001, True, 8), (1024, "bf16", 20001, True, 8), (1024, "bf16", 1, False, 0),
 ])
 def test_hadamard_smooth_quant_parity(qv, dev, K, dtype, M, smooth, pad):
     X = synth.vggt_activations(M, K, seed=K + M, dtype=dtype)
@@ -127,20 +127,24 @@ def test_constructed_ties_are_bit_exact(qv, dev, K, dtype):
 
 
 @pytest.mark.parametrize("K", [1024, 4096])
-def test_zero_tiny_and_outlier_rows(qv, dev, K):
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])  # bf16 rows take the matrix-core kernel
+def test_zero_tiny_and_outlier_rows(qv, dev, K, dtype):
     X = np.zeros((6, K), np.float32)
-    X[1, :] = 1e-41            # subnormal row: scale would be subnormal -> all-zero row
+    X[1, :] = 1e-41 if dtype == "fp32" else 1e-39  # subnormal row: subnormal scale -> all-zero row
     X[2, 17] = 1000.0          # one-hot outlier: spreads flat, every code +-7
     X[3, :] = 2.5              # constant row: a single spike
-    X[4] = synth.vggt_activations(1, K, seed=1)[0]
+    X[4] = synth.vggt_activations(1, K, seed=1, dtype=dtype)[0]
     X[5, ::2] = -3.0
-    q, s = run_quant(qv, dev, X, "fp32", None)
+    if dtype == "bf16":
+        X = synth.round_to_bf16(X)
+        assert X[1, 0] != 0 and abs(X[1, 0]) < 2.0 ** -126  # still a (bf16) subnormal
+    q, s = run_quant(qv, dev, X, dtype, None)
     assert s[0] == 0 and s[1] == 0
     codes = oracle.unpack_int4(q)
     assert np.all(codes[0] == 0) and np.all(codes[1] == 0)
     assert np.all(np.abs(codes[2]) == 7)
     assert codes[3, 0] == 7 and np.all(codes[3, 1:] == 0)
-    check_quant_against_oracle(X, None, q, s, oracle.ROT_EXPLICIT, f"special rows K={K}")
+    check_quant_against_oracle(X, None, q, s, oracle.ROT_EXPLICIT, f"special rows K={K} {dtype}")
 
 
 # ---------------------------------------------------------------------------- int4 GEMM
