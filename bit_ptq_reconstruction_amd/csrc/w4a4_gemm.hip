@@ -502,8 +502,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
   // Output stores.  The wave's block of rows m0 + wm*WM + (0..WM-1) is written through a buffer
   // resource that starts at the block's first output and ends after its last row below M: a store
   // to a row at or past M falls outside the range and is dropped, so the lanes need no bounds test
-  // and no 64-bit address; the row offset of a pass is a scalar operand.  The host admits output
-  // rows below 2^24 bytes, so the block's WM <= 128 rows span less than 2^31 bytes.
+  // and no 64-bit address.  The range check covers the vector offset (plus the instruction
+  // offset) only -- the scalar offset is added after it -- so the row of a pass goes into the
+  // vector offset too.  The host admits output rows below 2^24 bytes, so the block's WM <= 128 rows
+  // span less than 2^31 bytes.
   static_assert(WM <= 128, "32-bit output offsets");
   const int64_t row_stride = ldy * (int64_t)sizeof(OutT);
   const int64_t rows_left = M - (m0 + wm * WM);
@@ -516,7 +518,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
   // Row ru + lane / kChunksPerRow of the block (ru uniform), chunk lane % kChunksPerRow.
   auto store_out = [&](int ru, const u32x4& v) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_buffer_store_b128(v, yrsrc, lane_off, (uint32_t)(ru * row_stride), 2 /* nt */);
+    __builtin_amdgcn_raw_buffer_store_b128(v, yrsrc, lane_off + (uint32_t)(ru * row_stride), 0, 2 /* nt */);
 #else
     (void)ru; (void)v; (void)rows;  // the host pass compiles no kernel code
 #endif
@@ -637,8 +639,15 @@ hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const
 template <int BN, int BM, int WGN, int WGM, bool kBF16Out, bool kGelu, bool kBias, bool kW8>
 hipError_t launch_cfg(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
                       int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
-  // 128 codes (64 bytes of every row) per stage; a 256-code stage variant is kept selectable for
-  // measurements (it halves the barriers but its 64 KB ring leaves two blocks per CU).
+  // int4: 128 codes (64 bytes of every row) per stage; a 256-code stage variant is kept selectable
+  // for measurements (it halves the barriers but its 64 KB ring leaves two blocks per CU).
+  // int8: 128 codes (128 bytes) per stage where K allows; 64-byte stages would carry half the MFMA
+  // work per barrier, and measured 5 % slower on the block despite the four blocks per CU.
+  if constexpr (kW8) {
+    if ((K % 128) == 0)
+      return launch_t<BN, BM, WGN, WGM, 128, QV_STAGES_128, kBF16Out, kGelu, kBias, kW8>(Xq, xs, Wq, ws, bias, M, N, K,
+                                                                                      Y, ldy, st);
+  }
   if constexpr (QV_RB128 && !kW8) {
     if ((K % 256) == 0)
       return launch_t<BN, BM, WGN, WGM, 128, QV_STAGES_128, kBF16Out, kGelu, kBias, kW8>(Xq, xs, Wq, ws, bias, M, N, K,

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 import acceptance as acc
+from guard import check_guard, guarded_output
 import oracle
 from bit_ptq_reconstruction_amd import synth
 
@@ -120,10 +121,11 @@ def random_packed(rows, K, rng):
 
 def run_gemm_grouped(qv, dev, Xq, xs, Wq, ws, group, bias=None, epi=0, out="fp32"):
     M, N = Xq.shape[0], Wq.shape[0]
-    Y = torch.full((M, N), float("nan"), dtype=torch.float32 if out == "fp32" else torch.bfloat16, device=dev)
+    Yfull, Y = guarded_output(M, N, torch.float32 if out == "fp32" else torch.bfloat16, dev)
     qv.qv_w4a4_gemm_grouped(t_(Xq, dev), t_(xs, dev), t_(Wq, dev), t_(ws, dev), None if bias is None else t_(bias, dev),
                             Y, group, epi)
     torch.cuda.synchronize()
+    check_guard(Yfull, M, N, f"grouped gemm M={M} N={N}")
     return Y.float().cpu().numpy()
 
 

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import acceptance as acc
+from guard import check_guard, guarded_output
 import oracle
 from bit_ptq_reconstruction_amd import synth
 
@@ -160,14 +161,11 @@ def run_gemm(qv, dev, Xq, xs, Wq, ws, bias=None, epi=0, out="fp32", ldy_pad=0):
     M, N = Xq.shape[0], Wq.shape[0]
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     ydt = torch.float32 if out == "fp32" else torch.bfloat16
-    Yfull = torch.full((M, N + ldy_pad), float("nan"), dtype=ydt, device=dev)
-    Y = Yfull[:, :N]
+    Yfull, Y = guarded_output(M, N, ydt, dev, ldy_pad)
     qv.qv_w4a4_gemm(t(Xq), t(xs), t(Wq), t(ws), None if bias is None else t(bias), Y, epi)
     torch.cuda.synchronize()
-    out_np = Y.float().cpu().numpy()
-    if ldy_pad:
-        assert torch.isnan(Yfull[:, N:].float()).all(), "wrote outside the output rows"
-    return out_np
+    check_guard(Yfull, M, N, f"gemm M={M} N={N}")
+    return Y.float().cpu().numpy()
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (37, 256, 1024), (1374, 1024, 1024), (130, 128, 4096),
@@ -237,9 +235,10 @@ def test_gemm_many_tiles_per_block(qv, dev, K, epi, bias):
     ws = rng.uniform(0.01, 0.1, N).astype(np.float32)
     b = rng.standard_normal(N).astype(np.float32) if bias else None
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    Yfull, Y = guarded_output(M, N, torch.bfloat16, dev)
     qv.qv_w4a4_gemm(t(Xq), t(xs), t(Wq), t(ws), None if b is None else t(b), Y, epi)
     torch.cuda.synchronize()
+    check_guard(Yfull, M, N, "many tiles")
     rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 200, M), rng.choice(M, 300, replace=False)]))
     Yr = Y[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
     Y_ref = oracle.w4a4_gemm(Xq[rows], xs[rows], Wq, ws, b, epi)
