@@ -28,7 +28,9 @@
 // accumulators are dequantized into fp32 accumulators after the group's last stage.
 // MFMA operand roles: A = weight tile (output rows i = n), B = activation tile (columns j = m): a
 // lane owns runs of four consecutive n of one m; the epilogue stages each wave's outputs in LDS and
-// writes whole 128-byte row segments with 16-byte stores.  Tiles are assigned XCD-major: the
+// writes whole 128-byte row segments with 16-byte buffer stores whose range ends at the last row
+// below M.  With int8 operands (kW8) a stage holds 128 codes (128 bytes per row) where K allows,
+// and there is no widening.  Tiles are assigned XCD-major: the
 // hardware deals blocks round-robin over the 8 XCDs, and the block -> tile map gives each XCD a
 // contiguous run of tiles sharing activation rows.
 #include <hip/hip_runtime.h>
