@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import acceptance as acc
-from guard import check_guard, guarded_output
+from guard import check_codes_guard, check_guard, guarded_codes, guarded_output
 import oracle
 from bit_ptq_reconstruction_amd import synth
 
@@ -54,14 +54,15 @@ def smoothing_for(X, W):
 def quant_grouped(qv, dev, X, dtype, mult, group, weights=False):
     R, K = X.shape
     Xd = to_dev(X, dtype, dev)
-    q = torch.empty((R, K // 2), dtype=torch.uint8, device=dev)
-    s = torch.full((R, K // group), float("nan"), dtype=torch.float32, device=dev)
+    qfull, q, sfull, s = guarded_codes(R, K // 2, K // group, dev)
+    s.fill_(float("nan"))
     m = None if mult is None else t_(mult.astype(np.float32), dev)
     if weights:
         qv.qv_pack_weights_grouped(Xd, m, group, q, s)
     else:
         qv.qv_hadamard_smooth_quant_grouped(Xd, m, group, q, s)
     torch.cuda.synchronize()
+    check_codes_guard(qfull, sfull, R, label=f"grouped rotate-quantize R={R} K={K}")
     Xin = Xd.float().cpu().numpy().astype(np.float64)  # the values the kernel read (bf16-rounded)
     return q.cpu().numpy(), s.cpu().numpy(), Xin
 

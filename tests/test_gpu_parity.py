@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import acceptance as acc
-from guard import check_guard, guarded_output
+from guard import check_codes_guard, check_guard, guarded_codes, guarded_output
 import oracle
 from bit_ptq_reconstruction_amd import synth
 
@@ -52,10 +52,10 @@ def run_quant(qv, dev, X, dtype, mult, ld_pad=0, weights=False):
     if ld_pad:
         Xd = Xd[:, :K]
     md = None if mult is None else torch.from_numpy(mult).to(dev)
-    q = torch.full((M, K // 2), 0xAB, dtype=torch.uint8, device=dev)
-    s = torch.full((M,), -1.0, dtype=torch.float32, device=dev)
+    qfull, q, sfull, s = guarded_codes(M, K // 2, 0, dev)
     (qv.qv_pack_weights if weights else qv.qv_hadamard_smooth_quant)(Xd, md, q, s)
     torch.cuda.synchronize()
+    check_codes_guard(qfull, sfull, M, label=f"rotate-quantize M={M} K={K}")
     return q.cpu().numpy(), s.cpu().numpy()
 
 

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import acceptance as acc
-from guard import check_guard, guarded_output
+from guard import check_codes_guard, check_guard, guarded_codes, guarded_output
 import oracle
 from bit_ptq_reconstruction_amd import synth
 
@@ -43,11 +43,11 @@ def to_dev(a, dtype, dev):
 
 def run_quant8(qv, dev, X, dtype, mult, weights=False):
     M, K = X.shape
-    q = torch.full((M, K), 0x55, dtype=torch.int8, device=dev)
-    s = torch.full((M,), -1.0, dtype=torch.float32, device=dev)
+    qfull, q, sfull, s = guarded_codes(M, K, 0, dev, code_dtype=torch.int8, code_fill=0x55)
     md = None if mult is None else torch.from_numpy(mult).to(dev)
     (qv.qv_pack_weights8 if weights else qv.qv_hadamard_smooth_quant8)(to_dev(X, dtype, dev), md, q, s)
     torch.cuda.synchronize()
+    check_codes_guard(qfull, sfull, M, code_fill=0x55, label=f"rotate-quantize8 M={M} K={K}")
     return q.cpu().numpy(), s.cpu().numpy()
 
 
