@@ -313,12 +313,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(K == 4
 // a-values held by the 16 lanes of a DPP row), a constant slice of H_32 the A operand (16 of the 32
 // output indices b'), and two MFMAs (q = 0, 1) give all 32 b'.  Output row m = 4 (l / 16) + r of
 // MFMA q is assigned b' = r + 4 q + 8 (l / 16), so a lane ends with the 8 consecutive channels
-// b' = 8 (l / 16) + e, e = 4 q + r: one packed dword.  The a-transform remains: the low bits of a sit
-// on lane bits (DPP butterflies, as in fwht_regs.h), the tile index J (3 bits) in registers.
-//   K = 1024: DPP-row position p = 4 t + a_lo holds row t of the wave's 4 and a_lo = p & 3;
-//             a = 4 J + a_lo (2 DPP stages, 3 in-lane stages);
-//   K = 4096: one row per wave, p holds a_lo = chunk_of_lane16(p); a = 16 J + a_lo (4 DPP stages,
-//             3 in-lane stages).
+// b' = 8 (l / 16) + e, e = 4 q + r: one packed dword.  The a-transform remains: with LA a-values
+// of each row on the 16 lanes of a DPP row (DPP-row position p = LA t + pp for row t of the wave's
+// 16 / LA, a = LA J + a_lo(pp)), the a_lo bits are DPP butterflies (as in fwht_regs.h) and the tile
+// index J is in registers.
+//   K = 1024, LA = 8: two rows per wave, 32 values per lane, 3 DPP and 2 in-lane stages;
+//   K = 4096, LA = 16: one row per wave, 64 values per lane, 4 DPP and 3 in-lane stages.
 // Every element of the MFMA sum is an exact product and the fp32 accumulation of the 32 terms
 // stays within the rounding error of the five butterfly stages it replaces.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
