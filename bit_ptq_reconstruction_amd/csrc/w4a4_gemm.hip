@@ -69,7 +69,7 @@ constexpr int kXcds = 8;
 #define QV_BUF_DMA 1  // 1: stage loads through buffer resources (scalar stage offset); 0: global addresses
 #endif
 // Word 3 of a raw buffer resource on gfx9-class GPUs (32-bit data format, no swizzle).
-constexpr int kBufDword3 = 0x00020000;
+[[maybe_unused]] constexpr int kBufDword3 = 0x00020000;
 
 // Position inside an XCD's run -> offset in the run's canonical (row-major over tiles) order.
 // G = 0 keeps the canonical order: the blocks in flight share a few activation rows and sweep every
@@ -522,7 +522,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_raw_buffer_store_b128(v, yrsrc, lane_off + (uint32_t)(ru * row_stride), 0, 2 /* nt */);
 #else
-    (void)ru; (void)v; (void)rows;  // the host pass compiles no kernel code
+    (void)ru; (void)v; (void)rows; (void)row_stride; (void)Y;  // the host pass compiles no kernel code
 #endif
   };
 
