@@ -148,6 +148,27 @@ def test_zero_tiny_and_outlier_rows(qv, dev, K, dtype):
     check_quant_against_oracle(X, None, q, s, oracle.ROT_EXPLICIT, f"special rows K={K} {dtype}")
 
 
+@pytest.mark.parametrize("K", [1024, 4096])
+def test_cancellation_rows(qv, dev, K):
+    """bf16 rows built so that the 32-element groups the matrix-core kernel contracts first cancel:
+    x_k = big * (-1)^popcount(k & pattern) (1 + 2^-7 noise) + unit noise.  One output of each
+    32-point transform gathers the groups constructively; the other 31 are what is left of 32 large
+    terms of opposite signs, which is where fp32 summation order matters most."""
+    rng = np.random.default_rng(K + 11)
+    M = 48
+    k = np.arange(K)
+    X = np.empty((M, K), np.float32)
+    for m in range(M):
+        big = 10.0 ** rng.uniform(0, 4)
+        pattern = int(rng.integers(0, 32))
+        sign = np.where(np.array([bin(int(v) & pattern).count("1") % 2 for v in k]), -1.0, 1.0)
+        X[m] = big * sign * (1 + rng.standard_normal(K) * 2.0 ** -7) + rng.standard_normal(K)
+    X = synth.round_to_bf16(X)
+    q, s = run_quant(qv, dev, X, "bf16", None)
+    rate, _, _ = check_quant_against_oracle(X, None, q, s, oracle.ROT_EXPLICIT, f"cancellation rows K={K}")
+    print(f"cancellation rows K={K}: code mismatch rate {rate:.2e}")
+
+
 # ---------------------------------------------------------------------------- int4 GEMM
 
 def random_packed(rows, K, rng, fill=None):
