@@ -46,7 +46,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #ifndef QV_RQM_LANES_1024
 // a-values per DPP row of the width-1024 matrix-core kernel: 8 (2 rows per wave, 32 values per
 // lane, 96 registers, 5 waves) measured 5 % faster than the butterfly kernel; 4 (4 rows per wave,
-// 64 values, 151 registers, 3 waves) measured level with it.
+// 64 values, 151 registers, 3 waves) measured level with it, and 16 (one row per wave, 16 values,
+// 64 registers, 8 waves) 4-6 % slower than 8.
 #define QV_RQM_LANES_1024 8
 #endif
 #ifndef QV_RQM_WAVES_1024
