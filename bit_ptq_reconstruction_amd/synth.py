@@ -37,13 +37,6 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32)
 
 
-def bf16_bits(x: np.ndarray) -> np.ndarray:
-    """The uint16 bf16 encodings of fp32 values that are already bf16-representable."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    assert np.all((u & 0xFFFF) == 0), "values are not bf16-representable"
-    return (u >> 16).astype(np.uint16)
-
-
 def vggt_activations(M: int, K: int, seed: int, dtype: str = "fp32", first_row: int = 0) -> np.ndarray:
     """Rows [first_row, first_row + M) of the seeded activation stream, as fp32 values.
 
