@@ -285,8 +285,9 @@ def test_gemm_epilogue_parity(qv, dev, epi, out, bias, pad):
 
 # ---------------------------------------------------------------------------- whole layer
 
-def test_linear_equals_its_two_steps_and_is_deterministic(qv, dev):
-    M, K, N = 2000, 4096, 256
+@pytest.mark.parametrize("K", [1024, 4096])
+def test_linear_equals_its_two_steps_and_is_deterministic(qv, dev, K):
+    M, N = 2000, 256
     X = synth.vggt_activations(M, K, seed=9, dtype="bf16")
     W = synth.weights(N, K, seed=10)
     Xd, Wd = to_dev(X, "bf16", dev), to_dev(W, "fp32", dev)
@@ -308,6 +309,37 @@ def test_linear_equals_its_two_steps_and_is_deterministic(qv, dev):
     torch.cuda.synchronize()
     for Y2 in outs:
         assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+
+
+def test_calls_run_on_the_given_stream(qv, dev):
+    """Every call is ordered on the stream it is given: the whole layer issued on a side stream
+    (default priority), after that stream waited for the inputs, equals the default-stream result."""
+    M, K, N = 1500, 1024, 384
+    X = synth.vggt_activations(M, K, seed=12, dtype="bf16")
+    W = synth.weights(N, K, seed=13)
+    Xd, Wd = to_dev(X, "bf16", dev), to_dev(W, "fp32", dev)
+    sm = torch.ones(K, device=dev)
+    Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    ws = torch.empty((N,), dtype=torch.float32, device=dev)
+    qv.qv_pack_weights(Wd, sm, Wq, ws)
+    work = torch.empty((qv.qv_w4a4_linear_workspace_size(M, K),), dtype=torch.uint8, device=dev)
+    Y1 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    qv.qv_w4a4_linear(Xd, sm, Wq, ws, None, Y1, work, qv.QV_EPI_GELU)
+    torch.cuda.synchronize()
+    work2 = torch.empty_like(work)
+    Y2 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream())  # the inputs and Y2's fill are complete first
+    with torch.cuda.stream(side):
+        qv.qv_w4a4_linear(Xd, sm, Wq, ws, None, Y2, work2, qv.QV_EPI_GELU)
+        Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        xs = torch.empty((M,), dtype=torch.float32, device=dev)
+        Y3 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+        qv.qv_hadamard_smooth_quant(Xd, sm, Xq, xs, stream=side)
+        qv.qv_w4a4_gemm(Xq, xs, Wq, ws, None, Y3, qv.QV_EPI_GELU, stream=side)
+    side.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    assert torch.equal(Y1.view(torch.int16), Y3.view(torch.int16))
 
 
 def test_linear_against_oracle_end_to_end(qv, dev):
