@@ -29,7 +29,9 @@
  *   - Array arguments are DEVICE pointers, allocated and owned by the caller.  The library allocates
  *     nothing, frees nothing and keeps no pointer after returning.
  *   - hip_stream is a hipStream_t passed as void* (NULL = the default stream).  Every call is
- *     asynchronous and ordered on that stream; the library never synchronizes.
+ *     asynchronous and ordered on that stream; the library never synchronizes.  A call only
+ *     launches kernels (no allocation, memset, copy or synchronization), so calls may be recorded
+ *     into a HIP graph by stream capture and replayed.
  *   - All argument checks run on the host before any HIP call; a failed check returns its status and
  *     launches nothing.  M == 0 (or N == 0) is a valid no-op returning QV_OK.
  *   - Leading dimensions are in elements.  Base pointers must be 16-byte aligned and every row

@@ -342,6 +342,59 @@ def test_calls_run_on_the_given_stream(qv, dev):
     assert torch.equal(Y1.view(torch.int16), Y3.view(torch.int16))
 
 
+def test_calls_replay_from_a_hip_graph(qv, dev):
+    """The online calls record into a HIP graph (they launch kernels only: no memset, copy,
+    allocation or synchronisation). A two-layer chain (1024 -> 4096 with GELU, then the 4096-wide
+    rotation of that output -> 256) is captured once and replayed three times, with the outputs
+    overwritten and eager work between replays; every replay equals the eager result bit for bit."""
+    M, K1, N1, N2 = 2000, 1024, 4096, 256
+    X = to_dev(synth.vggt_activations(M, K1, seed=21, dtype="bf16"), "bf16", dev)
+    sm1, sm2 = torch.rand(K1, device=dev) + 0.5, torch.rand(N1, device=dev) + 0.5
+    Wq1 = torch.empty((N1, K1 // 2), dtype=torch.uint8, device=dev)
+    ws1 = torch.empty((N1,), dtype=torch.float32, device=dev)
+    Wq2 = torch.empty((N2, N1 // 2), dtype=torch.uint8, device=dev)
+    ws2 = torch.empty((N2,), dtype=torch.float32, device=dev)
+    qv.qv_pack_weights(to_dev(synth.weights(N1, K1, seed=22), "fp32", dev), sm1, Wq1, ws1)
+    qv.qv_pack_weights(to_dev(synth.weights(N2, N1, seed=23), "fp32", dev), sm2, Wq2, ws2)
+    Xq = torch.empty((M, K1 // 2), dtype=torch.uint8, device=dev)
+    xs = torch.empty((M,), dtype=torch.float32, device=dev)
+    Y1 = torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
+    Y2 = torch.empty((M, N2), dtype=torch.float32, device=dev)
+    work = torch.empty((qv.qv_w4a4_linear_workspace_size(M, N1),), dtype=torch.uint8, device=dev)
+
+    def chain():
+        qv.qv_hadamard_smooth_quant(X, 1.0 / sm1, Xq, xs)
+        qv.qv_w4a4_gemm(Xq, xs, Wq1, ws1, None, Y1, qv.QV_EPI_GELU)
+        qv.qv_w4a4_linear(Y1, 1.0 / sm2, Wq2, ws2, None, Y2, work, qv.QV_EPI_NONE)
+
+    inv1, inv2 = 1.0 / sm1, 1.0 / sm2
+
+    def chain_fixed():  # the graph keeps the multipliers' addresses: no tensors made inside it
+        qv.qv_hadamard_smooth_quant(X, inv1, Xq, xs)
+        qv.qv_w4a4_gemm(Xq, xs, Wq1, ws1, None, Y1, qv.QV_EPI_GELU)
+        qv.qv_w4a4_linear(Y1, inv2, Wq2, ws2, None, Y2, work, qv.QV_EPI_NONE)
+
+    chain_fixed()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (Xq, xs, Y1, Y2)]
+    assert torch.isfinite(ref[3]).all()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain_fixed()
+    torch.cuda.synchronize()
+    for r in range(3):
+        chain()  # eager work between replays (same results, fresh multiplier tensors)
+        Xq.fill_(0x55)
+        xs.fill_(-1.0)
+        Y1.fill_(float("nan"))
+        Y2.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((Xq, xs, Y1, Y2), ref):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {r}"
+
+
 def test_linear_against_oracle_end_to_end(qv, dev):
     """Single 1024->1024 linear on one frame (M = 1374), fp32 in and out, smoothing from frame 0."""
     M, K, N = 1374, 1024, 1024
