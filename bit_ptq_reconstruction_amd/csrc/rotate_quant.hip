@@ -22,6 +22,8 @@
 #include <hip/hip_bf16.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fwht_regs.h"
 #include "qv_internal.h"
 
@@ -586,20 +588,27 @@ __global__ void zero_kernel(unsigned* __restrict__ p, int64_t n) {
 
 // Resident blocks per CU for a kernel (queried once per kernel and device) times the CU count:
 // the streaming kernels loop over row groups, so a grid of exactly the resident blocks keeps every
-// wave busy with prefetched rows and leaves no partial last round.
+// wave busy with prefetched rows and leaves no partial last round.  The cache holds one entry per
+// kernel instance (the template argument) and device below 16; callers on several host threads may
+// fill an entry concurrently, each storing the same value.  Higher device ordinals query every time.
 template <auto kKernel>
 int resident_grid() {
-  static int cached[16] = {0};  // one cache per kernel instance (the template argument) and device
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-  if (cached[dev] == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kKernel, kThreads, 0) != hipSuccess || per_cu < 1)
-      per_cu = 1;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    cached[dev] = per_cu * cus;
+  static std::atomic<int> cached[16];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const bool cacheable = dev >= 0 && dev < 16;
+  if (cacheable) {
+    const int hit = cached[dev].load(std::memory_order_relaxed);
+    if (hit > 0) return hit;
   }
-  return cached[dev];
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kKernel, kThreads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const int grid = per_cu * cus;
+  if (cacheable) cached[dev].store(grid, std::memory_order_relaxed);
+  return grid;
 }
 
 int grid_for_rows(int64_t M, int rows_per_wave, int resident) {

@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "qv_internal.h"
@@ -611,15 +612,19 @@ hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const
   // Group-wise scales take one (BN + BM)-float slot per group, at most kMaxGroups of them.
   const size_t lds = kGS > 0 ? Lds::kScaleOffset + 4 * (size_t)(BN + BM) * (size_t)(K / (128 * kGS)) : Lds::kTotal;
   constexpr size_t kLdsMax = kGS > 0 ? Lds::kScaleOffset + 4 * (size_t)(BN + BM) * kMaxGroups : Lds::kTotal;
-  static int attr_set[16] = {0};  // per device: allow more than 64 KB of dynamic LDS once
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-  if (!attr_set[dev]) {
+  // Allow more than 64 KB of dynamic LDS, once per kernel instance and device below 16 (every
+  // call on higher device ordinals).  Concurrent first calls from several host threads each set
+  // the same attribute.
+  static std::atomic<bool> attr_set[16];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const bool cacheable = dev >= 0 && dev < 16;
+  if (!cacheable || !attr_set[dev].load(std::memory_order_relaxed)) {
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias, kW8, kGS>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
     if (e != hipSuccess) return e;
-    attr_set[dev] = 1;
+    if (cacheable) attr_set[dev].store(true, std::memory_order_relaxed);
   }
   const int64_t blocks = (N / BN) * ((M + BM - 1) / BM);
   hipLaunchKernelGGL((w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias, kW8, kGS>),
