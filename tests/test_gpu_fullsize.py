@@ -106,7 +106,7 @@ def check_rows(L, rows, X_rows, inv, Wcodes, ws_ref, label, dX=None):
     return rate, worst, Y_ref
 
 
-def full_size_linear(qv, dev, wl, lin, M, x_seed, w_seed):
+def full_size_linear(qv, dev, wl, lin, M, x_seed, w_seed, extra_rows=()):
     in_dt = workload.torch_dtype(wl.in_dtype)
     X = synth.vggt_activations_torch(M, lin.K, x_seed, in_dt, dev)
     W_host = synth.weights(lin.N, lin.K, w_seed)
@@ -116,7 +116,7 @@ def full_size_linear(qv, dev, wl, lin, M, x_seed, w_seed):
     torch.cuda.synchronize()
     label = f"{wl.name}/{lin.name} M={M} K={lin.K} N={lin.N}"
     Wcodes, ws_ref, wrate = check_weights(L, W_host, s, label)
-    rows = sample_rows(M, x_seed)
+    rows = np.union1d(sample_rows(M, x_seed), np.asarray(extra_rows, dtype=np.int64))
     X_rows = host(X[torch.from_numpy(rows).to(dev)])
     rate, worst, _ = check_rows(L, rows, X_rows, inv, Wcodes, ws_ref, label)
     print(f"{label}: weight mismatch {wrate:.1e}, row mismatch {rate:.1e} over {len(rows)} rows, "
@@ -130,6 +130,22 @@ def test_full_size_linears(qv, dev, name):
     for lin in wl.linears:
         x_seed, w_seed = workload.seeds(wl, lin, 0)
         full_size_linear(qv, dev, wl, lin, wl.M, x_seed, w_seed)
+        torch.cuda.empty_cache()
+
+
+def test_tensors_beyond_4_gib(qv, dev):
+    """600000 token rows (about 437 frames), beyond every workload.  fc2's bf16 input (width 4096)
+    spans 4.9 GB, so the rotate-quantize reads rows past byte offset 2^32; fc1's bf16 output (4096
+    columns) spans 4.9 GB, so the GEMM writes rows past it.  In both tensors row 524288 starts at
+    exactly 2^32 bytes: the rows on either side of it are checked with the sampled rows."""
+    wl = configs.WORKLOADS["block_32frames"]
+    M = 600000
+    boundary = (1 << 32) // (4096 * 2)
+    for lin in wl.linears:
+        if lin.name not in ("fc1", "fc2"):
+            continue
+        x_seed, w_seed = workload.seeds(wl, lin, 0)
+        full_size_linear(qv, dev, wl, lin, M, x_seed, w_seed, extra_rows=range(boundary - 6, boundary + 6))
         torch.cuda.empty_cache()
 
 
