@@ -395,6 +395,43 @@ def test_calls_replay_from_a_hip_graph(qv, dev):
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {r}"
 
 
+def test_calls_from_several_host_threads(qv, dev):
+    """Four host threads issue the layer concurrently, each on its own stream (default priority)
+    with its own workspace and output; every result equals the single-threaded one bit for bit.
+    The library's only host state is its per-device launch caches, which are atomics."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    M, K, N = 1500, 4096, 256
+    X = to_dev(synth.vggt_activations(M, K, seed=31, dtype="bf16"), "bf16", dev)
+    inv = 1.0 / (torch.rand(K, device=dev) + 0.5)
+    Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    ws = torch.empty((N,), dtype=torch.float32, device=dev)
+    qv.qv_pack_weights(to_dev(synth.weights(N, K, seed=32), "fp32", dev), 1.0 / inv, Wq, ws)
+    nbytes = qv.qv_w4a4_linear_workspace_size(M, K)
+    ref = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    qv.qv_w4a4_linear(X, inv, Wq, ws, None, ref, torch.empty((nbytes,), dtype=torch.uint8, device=dev),
+                      qv.QV_EPI_GELU)
+    torch.cuda.synchronize()
+    jobs = []
+    for _ in range(4):
+        Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+        work = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+        stream = torch.cuda.Stream(device=dev)
+        stream.wait_stream(torch.cuda.current_stream())  # inputs and the NaN fill are complete first
+        jobs.append((Y, work, stream))
+
+    def run(job):
+        Y, work, stream = job
+        for _ in range(10):
+            qv.qv_w4a4_linear(X, inv, Wq, ws, None, Y, work, qv.QV_EPI_GELU, stream=stream)
+        stream.synchronize()
+
+    with ThreadPoolExecutor(len(jobs)) as pool:
+        list(pool.map(run, jobs))
+    for Y, _, _ in jobs:
+        assert torch.equal(Y.view(torch.int16), ref.view(torch.int16))
+
+
 def test_linear_against_oracle_end_to_end(qv, dev):
     """Single 1024->1024 linear on one frame (M = 1374), fp32 in and out, smoothing from frame 0."""
     M, K, N = 1374, 1024, 1024
