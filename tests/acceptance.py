@@ -97,19 +97,30 @@ def bf16_round(y):
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+BF16_SUBNORMAL_STEP = 2.0 ** -133
+
+
+def bf16_ulp(r):
+    """The spacing of bf16 values in the binade of r: 2^(floor(log2 |r|) - 7) for normal r (8
+    significant bits), and the subnormal step 2^-133 below the normal range and at zero."""
+    r = np.abs(np.asarray(r, dtype=np.float64))
+    _, e = np.frexp(r)  # r = f * 2^e with f in [0.5, 1), so floor(log2 r) = e - 1 (frexp(0) gives e = 0)
+    return np.where(r > 0, np.maximum(np.ldexp(1.0, e - 8), BF16_SUBNORMAL_STEP), BF16_SUBNORMAL_STEP)
+
+
 def check_outputs(y_gpu, y_ref, out_bf16: bool, label=""):
     """Returns the worst relative error (fp32 outputs) or the worst difference in bf16 ulps."""
     y_gpu = np.asarray(y_gpu, dtype=np.float64)
     y_ref = np.asarray(y_ref, dtype=np.float64)
     if out_bf16:
         r = bf16_round(y_ref)
-        ulp = np.abs(r) * 2.0 ** -7  # one bf16 ulp at this magnitude (upper bound)
-        bad = np.abs(y_gpu - r) > ulp + 1e-38
+        ulp = bf16_ulp(r)
+        bad = np.abs(y_gpu - r) > ulp
         assert not np.any(bad), (f"{label}: {int(bad.sum())} bf16 outputs beyond 1 ulp, e.g. "
                                  f"{[(float(y_gpu[tuple(i)]), float(y_ref[tuple(i)])) for i in np.argwhere(bad)[:3]]}")
         # Reported: the largest difference from the rounded reference, in bf16 ulps at its magnitude.
         with np.errstate(divide="ignore", invalid="ignore"):
-            ulps = np.where(np.abs(y_gpu - r) > 0, np.abs(y_gpu - r) / np.maximum(ulp, 1e-38), 0.0)
+            ulps = np.where(np.abs(y_gpu - r) > 0, np.abs(y_gpu - r) / ulp, 0.0)
         return float(np.max(ulps)) if y_ref.size else 0.0
     with np.errstate(divide="ignore", invalid="ignore"):
         rel = np.abs(y_gpu - y_ref) / np.abs(y_ref)
@@ -177,7 +188,7 @@ def check_outputs_grouped(y_gpu, y_ref, y_abs, out_bf16: bool, groups: int, labe
     extra = 1.2 * 2.0 * (groups + 3) * U * np.asarray(y_abs, dtype=np.float64)
     if out_bf16:
         r = bf16_round(y_ref)
-        allow = np.abs(r) * 2.0 ** -7 + extra + 1e-38
+        allow = bf16_ulp(r) + extra
         err = np.abs(y_gpu - r)
     else:
         allow = OUT_REL_MAX * np.abs(y_ref) + extra + float(FLT_MIN32)

@@ -248,11 +248,16 @@ def test_gelu_identities(oracle_mod):
 
 
 def test_dequant_small_example(oracle_mod):
-    acc = np.array([[3, -4], [0, 49]], np.int32)
+    """Worked by hand: y[m][n] = acc[m][n] * sa[m] * sw[n] + bias[n].  The scales are chosen so that
+    no off-diagonal product sa[m] * sw[n] equals sa[n] * sw[m] (0.5 * 3 != 2 * 0.25), and the shape
+    is not square, so an index swap or a transposed operand changes the result."""
+    acc = np.array([[3, -4, 7], [5, 49, -1]], np.int32)
     sa = np.array([0.5, 2.0], np.float32)
-    sw = np.array([0.25, 1.0], np.float32)
-    Y = O.dequant(acc, sa, sw, bias=np.array([1.0, -1.0], np.float32))
-    np.testing.assert_array_equal(Y, [[3 * 0.125 + 1, -4 * 0.5 - 1], [0 + 1, 49 * 2.0 - 1]])
+    sw = np.array([0.25, 3.0, 0.125], np.float32)
+    Y = O.dequant(acc, sa, sw, bias=np.array([1.0, -1.0, 0.5], np.float32))
+    np.testing.assert_array_equal(Y, [[3 * 0.125 + 1, -4 * 1.5 - 1, 7 * 0.0625 + 0.5],
+                                      [5 * 0.5 + 1, 49 * 6.0 - 1, -1 * 0.25 + 0.5]])
+    np.testing.assert_array_equal(Y, [[1.375, -7.0, 0.9375], [3.5, 293.0, 0.25]])
 
 
 def test_pipeline_gemm_equals_steps(oracle_mod):

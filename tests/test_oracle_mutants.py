@@ -25,6 +25,8 @@ MUTANTS = {
     "unpack_no_sign_extension": ("if (lo >= 8) lo -= 16;", ""),
     "gemm_transposed_weight": ("(int64_t)qw[n * K + k];", "(int64_t)qw[k * N + n];"),
     "dequant_drops_bias": ("if (bias) y += (double)bias[n];", ""),
+    "dequant_scale_index_swap": ("double y = (double)acc[m * N + n] * (double)sa[m] * (double)sw[n];",
+                                 "double y = (double)acc[m * N + n] * (double)sa[n % M] * (double)sw[m % N];"),
     "gelu_wrong_sign": ("return 0.5 * y * erfc(-y / sqrt(2.0));", "return 0.5 * y * erfc(y / sqrt(2.0));"),
     "grouped_scale_ignores_group": ("y += (double)acc * (double)sa[m * groups + g] * (double)sw[n * groups + g];",
                                     "y += (double)acc * (double)sa[m * groups + g] * (double)sw[n * groups];"),
