@@ -12,6 +12,9 @@
 namespace {
 
 constexpr int64_t kAlign = 16;
+// Largest row count or leading dimension accepted (2^40): far beyond any device memory, and small
+// enough that every byte count formed from them below stays inside int64 / size_t.
+constexpr int64_t kMaxDim = int64_t{1} << 40;
 
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
 
@@ -23,12 +26,13 @@ bool valid_dtype(qv_dtype t) { return t == QV_F32 || t == QV_BF16; }
 qv_status check_rotate_quant(const void* X, qv_dtype dt, int64_t rows, int64_t K, int64_t ld, const float* mult,
                              const void* q, const float* scale) {
   if (!valid_dtype(dt)) return QV_ERR_DTYPE;
-  if (rows < 0 || K <= 0) return QV_ERR_SHAPE;
+  if (rows < 0 || K <= 0 || rows > kMaxDim) return QV_ERR_SHAPE;
   if (K != 1024 && K != 4096) return QV_ERR_UNSUPPORTED;
-  if (ld < K) return QV_ERR_SHAPE;
+  if (ld < K || ld > kMaxDim) return QV_ERR_SHAPE;
   if (rows == 0) return QV_OK;
   if (!X || !q || !scale) return QV_ERR_NULL;
-  if (!aligned(X) || !aligned(q) || !aligned(mult) || ((ld * dtype_bytes(dt)) % kAlign) != 0) return QV_ERR_ALIGN;
+  if (!aligned(X) || !aligned(q) || !aligned(scale) || !aligned(mult) || ((ld * dtype_bytes(dt)) % kAlign) != 0)
+    return QV_ERR_ALIGN;
   return QV_OK;
 }
 
@@ -37,14 +41,14 @@ qv_status check_gemm(const void* Xq, const float* xs, const void* Wq, const floa
                      int64_t M, int64_t N, int64_t K, qv_epilogue epi, const void* Y, qv_dtype yt, int64_t ldy,
                      int64_t k_step = 128) {
   if (!valid_dtype(yt) || (epi != QV_EPI_NONE && epi != QV_EPI_GELU)) return QV_ERR_DTYPE;
-  if (M < 0 || N < 0 || K <= 0) return QV_ERR_SHAPE;
+  if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim) return QV_ERR_SHAPE;
   if ((K % k_step) != 0 || K > 65536 || (N % 128) != 0) return QV_ERR_UNSUPPORTED;
   if (ldy < N) return QV_ERR_SHAPE;
   // output rows below 16 MiB: the epilogue addresses a tile's rows with 32-bit offsets
-  if (ldy * dtype_bytes(yt) >= (int64_t{1} << 24)) return QV_ERR_UNSUPPORTED;
+  if (ldy >= (int64_t{1} << 24) / dtype_bytes(yt)) return QV_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return QV_OK;
   if (!Xq || !xs || !Wq || !ws || !Y) return QV_ERR_NULL;
-  if (!aligned(Xq) || !aligned(Wq) || !aligned(ws) || !aligned(bias) || !aligned(Y) ||
+  if (!aligned(Xq) || !aligned(xs) || !aligned(Wq) || !aligned(ws) || !aligned(bias) || !aligned(Y) ||
       ((ldy * dtype_bytes(yt)) % kAlign) != 0)
     return QV_ERR_ALIGN;
   return QV_OK;
@@ -119,7 +123,7 @@ qv_status qv_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_t* W
 }
 
 size_t qv_w4a4_linear_workspace_size(int64_t M, int64_t K) {
-  if (M < 0 || K <= 0 || (K % 2) != 0) return 0;
+  if (M < 0 || K <= 0 || (K % 2) != 0 || M > kMaxDim || K > kMaxDim) return 0;
   return round256(static_cast<size_t>(M) * static_cast<size_t>(K / 2)) + round256(static_cast<size_t>(M) * 4);
 }
 
@@ -212,7 +216,7 @@ qv_status qv_w8a8_gemm(const int8_t* Xq8, const float* x_scale, const int8_t* Wq
 }
 
 size_t qv_w8a8_linear_workspace_size(int64_t M, int64_t K) {
-  if (M < 0 || K <= 0) return 0;
+  if (M < 0 || K <= 0 || M > kMaxDim || K > kMaxDim) return 0;
   return round256(static_cast<size_t>(M) * static_cast<size_t>(K)) + round256(static_cast<size_t>(M) * 4);
 }
 
@@ -291,7 +295,7 @@ qv_status qv_w4a4_gemm_grouped(const uint8_t* Xq, const float* x_scale, const ui
 }
 
 size_t qv_w4a4_linear_grouped_workspace_size(int64_t M, int64_t K, int64_t group) {
-  if (M < 0 || check_group(K, group) != QV_OK) return 0;
+  if (M < 0 || M > kMaxDim || check_group(K, group) != QV_OK) return 0;
   return round256(static_cast<size_t>(M) * static_cast<size_t>(K / 2)) +
          round256(static_cast<size_t>(M) * static_cast<size_t>(K / group) * 4);
 }

@@ -15,15 +15,43 @@ P = 0x100000  # a 16-byte-aligned dummy address: never dereferenced, because val
 P_MIS = P + 4
 
 
+# QV_ABI_TEST_LIB names a host-only build of the same ABI layer with stub launchers (built by
+# tests/test_sanitizers.py under AddressSanitizer and UndefinedBehaviorSanitizer).  The stubs count
+# launches, so in that build every rejected call is also checked to have launched nothing.
+STUB_LIB = os.environ.get("QV_ABI_TEST_LIB")
+
+
 @pytest.fixture(scope="module")
 def L():
     import bit_ptq_reconstruction_amd as qv
 
+    if STUB_LIB:
+        return qv.bind(ctypes.CDLL(STUB_LIB))
     if not os.path.exists(qv.library_path()):
         from bit_ptq_reconstruction_amd.build import build_library
 
         build_library()
     return qv.lib()
+
+
+@pytest.fixture(autouse=True)
+def no_launch_from_rejected_calls(request):
+    """With the stub build, the argument-error tests must not reach a launcher."""
+    if not STUB_LIB:
+        yield
+        return
+    L_ = request.getfixturevalue("L")
+    L_.qv_stub_reset()
+    yield
+    if request.node.name != "test_stub_counts_a_valid_call":
+        assert L_.qv_stub_launches() == 0, "a rejected call reached a kernel launcher"
+
+
+@pytest.mark.skipif(not STUB_LIB, reason="only meaningful in the host-only stub build")
+def test_stub_counts_a_valid_call(L):
+    """A fully valid call passes the checks and reaches the (stub) launcher once."""
+    assert hsq(L) == 7  # QV_ERR_HIP: the stub reports a launch failure
+    assert L.qv_stub_launches() == 1
 
 
 def declared_functions():
@@ -58,6 +86,9 @@ def test_workspace_size(L):
     assert qv.qv_w4a4_linear_workspace_size(1, 1024) == 512 + 256
     assert qv.qv_w4a4_linear_workspace_size(-1, 1024) == 0
     assert qv.qv_w4a4_linear_workspace_size(10, 0) == 0
+    assert qv.qv_w4a4_linear_workspace_size(1 << 62, 4096) == 0   # would wrap size_t
+    assert qv.qv_w8a8_linear_workspace_size(1 << 62, 4096) == 0
+    assert qv.qv_w4a4_linear_grouped_workspace_size(1 << 62, 4096, 128) == 0
 
 
 def hsq(L, X=P, dt=0, M=16, K=1024, ld=1024, mult=None, q=P, s=P):
@@ -78,9 +109,14 @@ def test_rotate_quant_argument_errors(L):
     assert hsq(L, X=P_MIS) == QV_ERR_ALIGN
     assert hsq(L, q=P_MIS) == QV_ERR_ALIGN
     assert hsq(L, mult=P_MIS) == QV_ERR_ALIGN
+    assert hsq(L, s=P_MIS) == QV_ERR_ALIGN           # the per-row scales
     assert hsq(L, dt=1, ld=1028) == QV_ERR_ALIGN      # bf16 row stride of 2056 bytes
     assert L.qv_pack_weights(P, 0, 8, 4096, 4095, None, P, P, None) == QV_ERR_SHAPE
     assert L.qv_pack_weights(P, 0, 8, 4096, 4096, None, None, P, None) == QV_ERR_NULL
+    # sizes whose byte counts would overflow 64 bits are rejected, not wrapped
+    assert hsq(L, M=1 << 62) == QV_ERR_SHAPE
+    assert hsq(L, ld=(1 << 62) + 1024) == QV_ERR_SHAPE
+    assert hsq(L, dt=1, ld=1 << 62) == QV_ERR_SHAPE
 
 
 def gemm(L, Xq=P, xs=P, Wq=P, ws=P, bias=None, M=16, N=128, K=1024, epi=0, Y=P, yt=0, ldy=128):
@@ -102,6 +138,8 @@ def test_gemm_argument_errors(L):
     assert gemm(L, Y=P_MIS) == QV_ERR_ALIGN
     assert gemm(L, bias=P_MIS) == QV_ERR_ALIGN
     assert gemm(L, Wq=P_MIS) == QV_ERR_ALIGN
+    assert gemm(L, xs=P_MIS) == QV_ERR_ALIGN          # token scales, read by the tile's scale fetch
+    assert gemm(L, ws=P_MIS) == QV_ERR_ALIGN
     assert gemm(L, yt=1, ldy=132) == QV_ERR_ALIGN     # bf16 row stride of 264 bytes
     # output rows of 2^24 bytes or more are outside the epilogue's 32-bit tile offsets
     # (M = 0: the shape checks run, nothing is launched)
@@ -109,6 +147,10 @@ def test_gemm_argument_errors(L):
     assert gemm(L, M=0, yt=1, ldy=1 << 23) == QV_ERR_UNSUPPORTED
     assert gemm(L, M=0, yt=0, ldy=(1 << 22) - 4) == QV_OK
     assert gemm(L, M=0, yt=1, ldy=(1 << 23) - 8) == QV_OK
+    # extreme sizes: rejected without forming an overflowing byte count
+    assert gemm(L, ldy=1 << 62) == QV_ERR_UNSUPPORTED
+    assert gemm(L, M=1 << 62) == QV_ERR_SHAPE
+    assert gemm(L, N=1 << 62, ldy=1 << 62) == QV_ERR_SHAPE
 
 
 def test_linear_argument_errors(L):
