@@ -18,13 +18,17 @@ import os
 __all__ = [
     "QVError", "QV_F32", "QV_BF16", "QV_EPI_NONE", "QV_EPI_GELU", "lib", "library_path",
     "qv_status_string", "qv_hadamard_smooth_quant", "qv_pack_weights", "qv_w4a4_gemm",
-    "qv_w4a4_linear_workspace_size", "qv_w4a4_linear", "qv_smooth_calibrate",
+    "qv_w4a4_linear_workspace_size", "qv_w4a4_linear", "qv_w4a4_linear_noalloc", "qv_smooth_calibrate",
+    "QV_NOALLOC_SCRATCH_BYTES",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libqv.so")
 
 QV_F32, QV_BF16 = 0, 1
+# Size of the library's static scratch array behind qv_w4a4_linear_noalloc (QV_NOALLOC_SCRATCH_BYTES
+# in include/qv.h).
+QV_NOALLOC_SCRATCH_BYTES = 32 << 20
 QV_EPI_NONE, QV_EPI_GELU = 0, 1
 
 _lib = None
@@ -61,6 +65,7 @@ def bind(L):
     L.qv_w4a4_linear_workspace_size.argtypes = [i64, i64]
     L.qv_w4a4_linear_workspace_size.restype = sz
     L.qv_w4a4_linear.argtypes = [P, i32, i64, i64, i64, P, P, P, P, i64, i32, P, i32, i64, P, sz, P]
+    L.qv_w4a4_linear_noalloc.argtypes = [P, i32, i64, i64, i64, P, P, P, P, i64, i32, P, i32, i64, P]
     L.qv_smooth_calibrate.argtypes = [P, i32, i64, i64, P, i32, i64, i64, i64, f32, P, P, P]
     L.qv_hadamard_smooth_quant8.argtypes = [P, i32, i64, i64, i64, P, P, P, P]
     L.qv_pack_weights8.argtypes = [P, i32, i64, i64, i64, P, P, P, P]
@@ -76,7 +81,7 @@ def bind(L):
     L.qv_w4a4_linear_grouped.argtypes = [P, i32, i64, i64, i64, P, i64, P, P, P, i64, i32, P, i32, i64, P, sz,
                                          P]
     for name in ("qv_hadamard_smooth_quant", "qv_pack_weights", "qv_w4a4_gemm", "qv_w4a4_linear",
-                 "qv_smooth_calibrate", "qv_hadamard_smooth_quant8", "qv_pack_weights8", "qv_w8a8_gemm",
+                 "qv_w4a4_linear_noalloc", "qv_smooth_calibrate", "qv_hadamard_smooth_quant8", "qv_pack_weights8", "qv_w8a8_gemm",
                  "qv_w8a8_linear", "qv_hadamard_smooth_quant_grouped", "qv_pack_weights_grouped",
                  "qv_w4a4_gemm_grouped", "qv_w4a4_linear_grouped"):
         getattr(L, name).restype = i32
@@ -243,6 +248,25 @@ def qv_w4a4_linear(X, inv_smooth, Wq, w_scale, bias, Y, workspace, epi: int = QV
     _check(lib().qv_w4a4_linear(_ptr(X), _dtype(X), M, K, _ld(X), _ptr(inv_smooth), _ptr(Wq), _ptr(w_scale),
                                 _ptr(bias), N, int(epi), _ptr(Y), _dtype(Y), _ld(Y), _ptr(workspace), nbytes,
                                 _stream(stream)), "qv_w4a4_linear")
+
+
+def qv_w4a4_linear_noalloc(X, inv_smooth, Wq, w_scale, bias, Y, epi: int = QV_EPI_NONE, stream=None) -> None:
+    """The whole online layer without a caller workspace: the codes and scales live in the library's
+    static device array (at most ``QV_NOALLOC_SCRATCH_BYTES`` of them).  Calls that overlap in time
+    on one GPU race on that array; calls on one stream are ordered."""
+    what = "qv_w4a4_linear_noalloc"
+    M, K = _rows_cols(what, "X", X)
+    N = _rows_cols(what, "Wq", Wq)[0]
+    _spec(what, "X", X, _FLOAT, (M, K), rows_packed=True)
+    _spec(what, "inv_smooth", inv_smooth, ("float32",), (K,), optional=True)
+    _spec(what, "Wq", Wq, ("uint8",), (N, K // 2))
+    _spec(what, "w_scale", w_scale, ("float32",), (N,))
+    _spec(what, "bias", bias, ("float32",), (N,), optional=True)
+    _spec(what, "Y", Y, _FLOAT, (M, N), rows_packed=True)
+    _same_gpu(what, X, inv_smooth, Wq, w_scale, bias, Y)
+    _check(lib().qv_w4a4_linear_noalloc(_ptr(X), _dtype(X), M, K, _ld(X), _ptr(inv_smooth), _ptr(Wq),
+                                        _ptr(w_scale), _ptr(bias), N, int(epi), _ptr(Y), _dtype(Y), _ld(Y),
+                                        _stream(stream)), what)
 
 
 def qv_smooth_calibrate(Xc, W, smooth, inv_smooth, alpha: float = 0.5, stream=None) -> None:

@@ -17,7 +17,7 @@ ARCH = "gfx950"
 # Packed-fp32 VALU forms are switched off for every device compile.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
-SOURCES = ["rotate_quant.hip", "w4a4_gemm.hip", "qv_abi.cpp"]
+SOURCES = ["rotate_quant.hip", "w4a4_gemm.hip", "noalloc_scratch.hip", "qv_abi.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -155,6 +155,38 @@ qv_status qv_w4a4_linear(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, 
   }
 }
 
+qv_status qv_w4a4_linear_noalloc(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                 const float* inv_smooth, const uint8_t* Wq, const float* w_scale, const float* bias,
+                                 int64_t N, qv_epilogue epi, void* Y, qv_dtype y_dtype, int64_t ldy,
+                                 void* hip_stream) {
+  try {
+    qv_status st = check_rotate_quant(X, x_dtype, M, K, ldx, inv_smooth, reinterpret_cast<uint8_t*>(16),
+                                      reinterpret_cast<float*>(16));
+    if (st != QV_OK) return st;
+    st = check_gemm(reinterpret_cast<uint8_t*>(16), reinterpret_cast<float*>(16), Wq, w_scale, bias, M, N, K, epi,
+                    Y, y_dtype, ldy);
+    if (st != QV_OK) return st;
+    if (M == 0 || N == 0) return QV_OK;
+    // The codes and scales must fit the static array (checked on the host, before any HIP call).
+    const size_t need = qv_w4a4_linear_workspace_size(M, K);
+    if (need == 0 || need > QV_NOALLOC_SCRATCH_BYTES) return QV_ERR_WORKSPACE;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    st = hip_status(qv::noalloc_scratch(&ws, &ws_bytes));
+    if (st != QV_OK) return st;
+    if (ws_bytes < need) return QV_ERR_WORKSPACE;
+    uint8_t* xq = static_cast<uint8_t*>(ws);
+    float* xs = reinterpret_cast<float*>(xq + round256(static_cast<size_t>(M) * static_cast<size_t>(K / 2)));
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    st = hip_status(qv::launch_rotate_quant(X, x_dtype == QV_BF16, M, K, ldx, inv_smooth, xq, xs, 4, s));
+    if (st != QV_OK) return st;
+    return hip_status(
+        qv::launch_w4a4_gemm(xq, xs, Wq, w_scale, bias, M, N, K, epi == QV_EPI_GELU, Y, y_dtype == QV_BF16, ldy, s));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
 qv_status qv_smooth_calibrate(const void* Xc, qv_dtype xc_dtype, int64_t Mc, int64_t ldx, const void* W,
                               qv_dtype w_dtype, int64_t N, int64_t ldw, int64_t K, float alpha, float* smooth,
                               float* inv_smooth, void* hip_stream) {

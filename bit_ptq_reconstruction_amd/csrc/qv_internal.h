@@ -2,6 +2,7 @@
 // Arguments are validated by the ABI layer (qv_abi.cpp) before any of these is called.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace qv {
@@ -35,6 +36,10 @@ hipError_t launch_w4a4_gemm_grouped(const uint8_t* Xq, const float* xs, const ui
 hipError_t launch_w8a8_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
                             const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out,
                             int64_t ldy, hipStream_t st);
+
+// Device address (on the current device) and size of the library's static scratch array, used
+// by qv_w4a4_linear_noalloc in place of a caller workspace.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 
 // Smoothing factors from rotated column maxima of calibration rows and weight rows.
 hipError_t launch_smooth_calibrate(const void* Xc, bool xbf16, int64_t Mc, int64_t ldx, const void* W, bool wbf16,

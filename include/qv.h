@@ -122,6 +122,30 @@ qv_status qv_w4a4_linear(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, 
                          const float* bias, int64_t N, qv_epilogue epi, void* Y, qv_dtype y_dtype,
                          int64_t ldy, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Bytes of the static device scratch array behind qv_w4a4_linear_noalloc, one copy per GPU. */
+#define QV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * qv_w4a4_linear_noalloc -- qv_w4a4_linear for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Arguments,
+ * rules and results are those of qv_w4a4_linear; the packed codes and per-row scales go to a
+ * static device array inside the library instead of a caller workspace.
+ *   Limit: qv_w4a4_linear_workspace_size(M, K) <= QV_NOALLOC_SCRATCH_BYTES (32 MiB), i.e. up to
+ *   65027 rows at K = 1024 and 16352 rows at K = 4096; larger calls return QV_ERR_WORKSPACE and
+ *   launch nothing.
+ *   The call allocates and frees nothing.  Each GPU the library runs on holds its own copy of the
+ *   array until the process ends; the first call on a device looks up that copy's device address
+ *   (hipGetSymbolAddress) and caches it.
+ *   Every call on one GPU uses that GPU's one array, which keeps the last call's contents (the
+ *   codes and scales are fully rewritten before they are read, so nothing needs clearing).  Calls
+ *   on one stream are ordered and safe; calls that overlap in time on one GPU (several streams,
+ *   several host threads) race on the array and give undefined results.
+ */
+qv_status qv_w4a4_linear_noalloc(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                 const float* inv_smooth, const uint8_t* Wq, const float* w_scale,
+                                 const float* bias, int64_t N, qv_epilogue epi, void* Y, qv_dtype y_dtype,
+                                 int64_t ldy, void* hip_stream);
+
 /*
  * qv_smooth_calibrate -- smoothing factors from rotated statistics ([P4] 后局部平滑: the factor is
  * computed from the distribution after the Hadamard rotation, alpha balances the two sides):

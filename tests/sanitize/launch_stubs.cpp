@@ -40,4 +40,6 @@ hipError_t launch_smooth_calibrate(const void*, bool, int64_t, int64_t, const vo
   return stub();
 }
 
+hipError_t noalloc_scratch(void**, size_t*) { return stub(); }
+
 }  // namespace qv

@@ -172,6 +172,38 @@ def test_linear_argument_errors(L):
     assert lin(M=0) == QV_OK
 
 
+def test_noalloc_linear_argument_errors(L):
+    """The allocation-free linear: the rules of qv_w4a4_linear, and sizes whose codes and scales
+    exceed the static array are rejected before any launch."""
+    import bit_ptq_reconstruction_amd as qv
+
+    text = open(HEADER).read()
+    m = re.search(r"#define QV_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == qv.QV_NOALLOC_SCRATCH_BYTES
+
+    def na(M=16, K=1024, ld=None, N=128, ldy=128, **kw):
+        a = dict(X=P, dt=1, inv=None, Wq=P, w_scale=P, bias=None, epi=0, Y=P, yt=1)
+        a.update(kw)
+        return L.qv_w4a4_linear_noalloc(a["X"], a["dt"], M, K, K if ld is None else ld, a["inv"], a["Wq"],
+                                        a["w_scale"], a["bias"], N, a["epi"], a["Y"], a["yt"], ldy, None)
+
+    assert na(M=0) == QV_OK
+    assert na(X=None) == QV_ERR_NULL
+    assert na(Wq=None) == QV_ERR_NULL
+    assert na(K=2048) == QV_ERR_UNSUPPORTED
+    assert na(N=100, ldy=100) == QV_ERR_UNSUPPORTED
+    assert na(Y=P_MIS) == QV_ERR_ALIGN
+    assert na(epi=3) == QV_ERR_DTYPE
+    # the largest row counts whose codes and scales fit 32 MiB, and one row more
+    assert L.qv_w4a4_linear_workspace_size(65027, 1024) <= qv.QV_NOALLOC_SCRATCH_BYTES
+    assert L.qv_w4a4_linear_workspace_size(65028, 1024) > qv.QV_NOALLOC_SCRATCH_BYTES
+    assert L.qv_w4a4_linear_workspace_size(16352, 4096) <= qv.QV_NOALLOC_SCRATCH_BYTES
+    assert L.qv_w4a4_linear_workspace_size(16353, 4096) > qv.QV_NOALLOC_SCRATCH_BYTES
+    assert na(M=65028) == QV_ERR_WORKSPACE
+    assert na(M=16353, K=4096) == QV_ERR_WORKSPACE
+    assert na(M=1 << 30, K=4096) == QV_ERR_WORKSPACE
+
+
 def test_calibrate_argument_errors(L):
     f = ctypes.c_float
 
