@@ -60,8 +60,11 @@ def run_linear(qv, L: Layer, stream=None) -> None:
         qv.qv_w4a4_gemm(L.Xq, L.xs, L.Wq, L.ws, None, L.Y, L.lin.epi, stream)
 
 
-def build(qv, wl: Workload, device, share_outputs: bool = False, bits: int = 4, group: int = 0):
+def build(qv, wl: Workload, device, share_outputs: bool = False, bits: int = 4, group: int = 0, inputs=None):
     """Allocate and prepare every layer of ``wl`` on ``device`` (timing inputs, seeded on device).
+
+    ``inputs``: layers of an earlier ``build`` of the same workload whose activation tensors are
+    reused (they are the same seeded draws), so a variant of a large workload holds no second copy.
 
     Activations are drawn per layer and per block.  With ``share_outputs`` the code/scale buffers
     and outputs are shared by the layers of equal shape across blocks (a 48-block stack would
@@ -94,7 +97,13 @@ def build(qv, wl: Workload, device, share_outputs: bool = False, bits: int = 4, 
         for li, lin in enumerate(wl.linears):
             x_seed, w_seed = seeds(wl, lin, blk)
             chained = wl.chain_mlp and li > 0
-            X = None if chained else synth.vggt_activations_torch(M, lin.K, x_seed, in_dt, device)
+            if chained:
+                X = None
+            elif inputs is not None:
+                X = inputs[len(layers)].X
+                assert X.shape == (M, lin.K) and X.dtype == in_dt
+            else:
+                X = synth.vggt_activations_torch(M, lin.K, x_seed, in_dt, device)
             W = synth.weights_torch(lin.N, lin.K, w_seed, device)
             s = torch.empty(lin.K, device=device)
             inv = torch.empty(lin.K, device=device)
