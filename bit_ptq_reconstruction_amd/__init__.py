@@ -19,7 +19,7 @@ __all__ = [
     "QVError", "QV_F32", "QV_BF16", "QV_EPI_NONE", "QV_EPI_GELU", "lib", "library_path",
     "qv_status_string", "qv_hadamard_smooth_quant", "qv_pack_weights", "qv_w4a4_gemm",
     "qv_w4a4_linear_workspace_size", "qv_w4a4_linear", "qv_w4a4_linear_noalloc", "qv_smooth_calibrate",
-    "QV_NOALLOC_SCRATCH_BYTES",
+    "QV_NOALLOC_SCRATCH_BYTES", "qv_w4a4_gemm_requant", "qv_w4a4_gemm_requant_workspace_size",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +66,9 @@ def bind(L):
     L.qv_w4a4_linear_workspace_size.restype = sz
     L.qv_w4a4_linear.argtypes = [P, i32, i64, i64, i64, P, P, P, P, i64, i32, P, i32, i64, P, sz, P]
     L.qv_w4a4_linear_noalloc.argtypes = [P, i32, i64, i64, i64, P, P, P, P, i64, i32, P, i32, i64, P]
+    L.qv_w4a4_gemm_requant_workspace_size.argtypes = [i64]
+    L.qv_w4a4_gemm_requant_workspace_size.restype = sz
+    L.qv_w4a4_gemm_requant.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P, i64, P, P, P, P, sz, P]
     L.qv_smooth_calibrate.argtypes = [P, i32, i64, i64, P, i32, i64, i64, i64, f32, P, P, P]
     L.qv_hadamard_smooth_quant8.argtypes = [P, i32, i64, i64, i64, P, P, P, P]
     L.qv_pack_weights8.argtypes = [P, i32, i64, i64, i64, P, P, P, P]
@@ -81,7 +84,7 @@ def bind(L):
     L.qv_w4a4_linear_grouped.argtypes = [P, i32, i64, i64, i64, P, i64, P, P, P, i64, i32, P, i32, i64, P, sz,
                                          P]
     for name in ("qv_hadamard_smooth_quant", "qv_pack_weights", "qv_w4a4_gemm", "qv_w4a4_linear",
-                 "qv_w4a4_linear_noalloc", "qv_smooth_calibrate", "qv_hadamard_smooth_quant8", "qv_pack_weights8", "qv_w8a8_gemm",
+                 "qv_w4a4_linear_noalloc", "qv_w4a4_gemm_requant", "qv_smooth_calibrate", "qv_hadamard_smooth_quant8", "qv_pack_weights8", "qv_w8a8_gemm",
                  "qv_w8a8_linear", "qv_hadamard_smooth_quant_grouped", "qv_pack_weights_grouped",
                  "qv_w4a4_gemm_grouped", "qv_w4a4_linear_grouped"):
         getattr(L, name).restype = i32
@@ -248,6 +251,29 @@ def qv_w4a4_linear(X, inv_smooth, Wq, w_scale, bias, Y, workspace, epi: int = QV
     _check(lib().qv_w4a4_linear(_ptr(X), _dtype(X), M, K, _ld(X), _ptr(inv_smooth), _ptr(Wq), _ptr(w_scale),
                                 _ptr(bias), N, int(epi), _ptr(Y), _dtype(Y), _ld(Y), _ptr(workspace), nbytes,
                                 _stream(stream)), "qv_w4a4_linear")
+
+
+def qv_w4a4_gemm_requant_workspace_size(M: int) -> int:
+    return int(lib().qv_w4a4_gemm_requant_workspace_size(int(M)))
+
+
+def qv_w4a4_gemm_requant(Xq, x_scale, Wq, w_scale, bias, Y, inv_smooth_next, Xq_next, x_scale_next, workspace,
+                         epi: int = QV_EPI_NONE, stream=None) -> None:
+    """Y [M, N] bf16 = dequant(Xq . Wq^T) (+ bias) (+ GELU), and Xq_next [M, N/2] / x_scale_next [M]: Y's
+    rows rotated at width N (1024 or 4096), smoothed by ``inv_smooth_next`` and quantized to int4, as
+    ``qv_hadamard_smooth_quant(Y, inv_smooth_next, ...)`` would give."""
+    what = "qv_w4a4_gemm_requant"
+    M, N, K = _check_gemm(what, Xq, x_scale, Wq, w_scale, bias, Y, "uint8", lambda c: 2 * c)
+    if _dtname(Y) != "bfloat16":
+        raise ValueError(f"{what}: Y must be bfloat16 (the next layer's input)")
+    _spec(what, "inv_smooth_next", inv_smooth_next, ("float32",), (N,), optional=True)
+    _spec(what, "Xq_next", Xq_next, ("uint8",), (M, N // 2))
+    _spec(what, "x_scale_next", x_scale_next, ("float32",), (M,))
+    _check_workspace(what, workspace, qv_w4a4_gemm_requant_workspace_size(M))
+    _same_gpu(what, Xq, x_scale, Wq, w_scale, bias, Y, inv_smooth_next, Xq_next, x_scale_next, workspace)
+    _check(lib().qv_w4a4_gemm_requant(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), _ptr(bias), M, N, K, int(epi),
+                                      _ptr(Y), _ld(Y), _ptr(inv_smooth_next), _ptr(Xq_next), _ptr(x_scale_next),
+                                      _ptr(workspace), workspace.numel(), _stream(stream)), what)
 
 
 def qv_w4a4_linear_noalloc(X, inv_smooth, Wq, w_scale, bias, Y, epi: int = QV_EPI_NONE, stream=None) -> None:

@@ -187,6 +187,34 @@ qv_status qv_w4a4_linear_noalloc(const void* X, qv_dtype x_dtype, int64_t M, int
   }
 }
 
+size_t qv_w4a4_gemm_requant_workspace_size(int64_t M) {
+  if (M < 0 || M > kMaxDim) return 0;
+  return round256(static_cast<size_t>((M + 127) / 128) * 4);
+}
+
+qv_status qv_w4a4_gemm_requant(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq, const float* w_scale,
+                               const float* bias, int64_t M, int64_t N, int64_t K, qv_epilogue epi, void* Y,
+                               int64_t ldy, const float* inv_smooth_next, uint8_t* Xq_next, float* x_scale_next,
+                               void* workspace, size_t workspace_bytes, void* hip_stream) {
+  try {
+    qv_status st = check_gemm(Xq, x_scale, Wq, w_scale, bias, M, N, K, epi, Y, QV_BF16, ldy);
+    if (st != QV_OK) return st;
+    if (N != 1024 && N != 4096) return QV_ERR_UNSUPPORTED;  // the next layer's Hadamard width
+    if (M == 0) return QV_OK;
+    if (!Xq_next || !x_scale_next) return QV_ERR_NULL;
+    if (!aligned(Xq_next) || !aligned(x_scale_next) || !aligned(inv_smooth_next)) return QV_ERR_ALIGN;
+    const size_t need = qv_w4a4_gemm_requant_workspace_size(M);
+    if (!workspace || workspace_bytes < need) return QV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) % 256) != 0) return QV_ERR_ALIGN;
+    return hip_status(qv::launch_w4a4_gemm_requant(Xq, x_scale, Wq, w_scale, bias, M, N, K, epi == QV_EPI_GELU, Y,
+                                                   ldy, inv_smooth_next, Xq_next, x_scale_next,
+                                                   static_cast<unsigned*>(workspace),
+                                                   static_cast<hipStream_t>(hip_stream)));
+  } catch (...) {
+    return QV_ERR_INTERNAL;
+  }
+}
+
 qv_status qv_smooth_calibrate(const void* Xc, qv_dtype xc_dtype, int64_t Mc, int64_t ldx, const void* W,
                               qv_dtype w_dtype, int64_t N, int64_t ldw, int64_t K, float alpha, float* smooth,
                               float* inv_smooth, void* hip_stream) {

@@ -19,6 +19,14 @@ hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* xs, const uint8_t* W
                             const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y, bool bf16_out,
                             int64_t ldy, hipStream_t st);
 
+// The int4 GEMM with bf16 outputs (N in {1024, 4096}) that also rotates, smooths (mult_next [N])
+// and quantizes every finished row stripe of its output for the next linear: q_next [M][N / 2],
+// scale_next [M].  counters: ceil(M / 128) unsigned of scratch, cleared by the call.
+hipError_t launch_w4a4_gemm_requant(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws,
+                                    const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y,
+                                    int64_t ldy, const float* mult_next, uint8_t* q_next, float* scale_next,
+                                    unsigned* counters, hipStream_t st);
+
 // Group-wise variant of the rotate-quantize step: one scale per row and group of `group` in
 // {128, 256, 512} channels, scale[row][K / group].
 hipError_t launch_rotate_quant_grouped(const void* X, bool bf16, int64_t M, int64_t K, int64_t ld, const float* mult,

@@ -40,6 +40,7 @@
 #include <type_traits>
 
 #include "qv_internal.h"
+#include "rq_mfma.h"
 
 namespace qv {
 
@@ -174,12 +175,27 @@ constexpr int waves_per_eu() {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
+// Next-layer quantization fused into the GEMM (kReq = N, the next layer's Hadamard width, 1024 or
+// 4096; 0 = none): the bf16 output rows are also rotated, smoothed and quantized for the next
+// linear ([P4] 预全局旋转 / 后局部平滑 / 训练后量化（PTQ） applied to this layer's output).  A row
+// needs all N outputs, which span the N / BN tiles of its row stripe.  Every block, after storing
+// its tile, makes its stores visible device-wide (agent-scope release) and increments the
+// stripe's counter; the block that brings the counter to N / BN -- the last tile of the stripe to
+// finish -- acquires and runs the rotate-quantize over the stripe's rows, reading them back
+// (mostly from the caches).  No block ever waits on another.
+struct NextQuant {
+  const float* mult;     // [N] per-channel factor of the next layer (1 / smoothing), or NULL
+  uint8_t* q;            // [M][N / 2] packed int4 codes of the next layer's input
+  float* scale;          // [M] per-row scales
+  unsigned* counters;    // [ceil(M / BM)] tile counts per row stripe, zero at launch
+};
+
 // kW8: int8 operands (one code per byte, no widening, the accumulator is acc itself) instead of
 // packed int4.  kGS > 0: group-wise scales, one per row and group of 128 kGS channels (kGS stages
 // of 128 codes): x_scale is [M][K / (128 kGS)], w_scale [N][K / (128 kGS)], and each group's int32
 // accumulator is dequantized into an fp32 accumulator when the group's last stage is done.
 template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias, bool kW8,
-          int kGS = 0>
+          int kGS = 0, int kReq = 0>
 __global__ __launch_bounds__(64 * WGN * WGM)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kGS>()))) void w4a4_gemm_kernel(const uint8_t* __restrict__ Xq,
                                                             const float* __restrict__ x_scale,
@@ -187,7 +203,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
                                                             const float* __restrict__ w_scale,
                                                             const float* __restrict__ bias, int64_t M,
                                                             int64_t N, int64_t K, void* __restrict__ Y,
-                                                            int64_t ldy) {
+                                                            int64_t ldy, NextQuant nq) {
   constexpr int kWaves = WGN * WGM, kThr = 64 * kWaves;
   constexpr int WN = BN / WGN, WM = BM / WGM;  // wave sub-tile
   constexpr int FN = WN / 32, FM = WM / 32;
@@ -521,7 +537,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
   // Row ru + lane / kChunksPerRow of the block (ru uniform), chunk lane % kChunksPerRow.
   auto store_out = [&](int ru, const u32x4& v) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_buffer_store_b128(v, yrsrc, lane_off + (uint32_t)(ru * row_stride), 0, 2 /* nt */);
+    // non-temporal, except where the next-layer quantization reads the rows back
+    __builtin_amdgcn_raw_buffer_store_b128(v, yrsrc, lane_off + (uint32_t)(ru * row_stride), 0, kReq ? 0 : 2);
 #else
     (void)ru; (void)v; (void)rows; (void)row_stride; (void)Y;  // the host pass compiles no kernel code
 #endif
@@ -602,12 +619,56 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
       store_out(pass * kRowsPerPass, v);
     }
   }
+
+  if constexpr (kReq > 0) {
+    static_assert(kBF16Out && !kW8 && kGS == 0 && (kReq == 1024 || kReq == 4096), "fused requantization: bf16 rows");
+    constexpr int LA = kReq == 1024 ? 8 : 16;
+    using RQ = MfmaRowQuant<kReq, 4, LA>;
+    using RL = typename RQ::L;
+    static_assert(RL::kTableRows * kCmStride * 4 <= (int)GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out>::kScaleOffset,
+                  "factor table fits the stage ring");
+    static_assert(BM % (kWaves * RL::kRowsPerWave) == 0, "whole row groups per wave");
+    // Every wave's output stores are complete and visible at agent scope, then one increment per block.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    int* const flag = reinterpret_cast<int*>(lds + GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out>::kScaleOffset);
+    if (tid == 0) {
+      const unsigned done = __hip_atomic_fetch_add(nq.counters + tile_m, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *flag = (done == (unsigned)(tiles_n - 1)) ? 1 : 0;
+    }
+    __syncthreads();
+    if (*flag == 0) return;  // uniform over the block
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other tiles' stores of this stripe are visible
+
+    // This block finished the stripe: rotate-quantize its rows m0 .. min(m0 + BM, M) - 1.
+    float* const cm = reinterpret_cast<float*>(lds);
+    fill_mfma_table<kReq, LA, kThr>(nq.mult, cm);
+    __syncthreads();
+    const RQ rq(lane);
+    const float* cm_row = rq.table_row(cm);
+    const uint16_t* const Yb = static_cast<const uint16_t*>(Y);
+    const int64_t m_end = (m0 + BM < M) ? m0 + BM : M;
+    constexpr int kGroupRows = kWaves * RL::kRowsPerWave;  // rows per step of the whole block
+    // At width 1024 the next row group's loads are issued before the current one is finished; at
+    // width 4096 (64 values per lane) that would not fit the GEMM's 128 registers.
+    constexpr bool kPrefetch = kReq == 1024;
+    rq_u32x4 raw[RQ::T];
+    int64_t r0 = m0 + wave * RL::kRowsPerWave;
+    if (kPrefetch && r0 < m_end) rq.load(Yb, ldy, r0, m_end, raw);
+    for (; r0 < m_end; r0 += kGroupRows) {
+      float v[RQ::T][8];
+      if (!kPrefetch) rq.load(Yb, ldy, r0, m_end, raw);
+      rq.transform_b(raw, v);
+      if (kPrefetch && r0 + kGroupRows < m_end) rq.load(Yb, ldy, r0 + kGroupRows, m_end, raw);
+      rq.finish(v, cm_row, r0, m_end, nq.q, nq.scale);
+    }
+  }
 }
 
 template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, bool kGelu, bool kBias, bool kW8,
-          int kGS = 0>
+          int kGS = 0, int kReq = 0>
 hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
-                    int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
+                    int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st, NextQuant nq = {}) {
   using Lds = GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out>;
   // Group-wise scales take one (BN + BM)-float slot per group, at most kMaxGroups of them.
   const size_t lds = kGS > 0 ? Lds::kScaleOffset + 4 * (size_t)(BN + BM) * (size_t)(K / (128 * kGS)) : Lds::kTotal;
@@ -621,14 +682,14 @@ hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const
   const bool cacheable = dev >= 0 && dev < 16;
   if (!cacheable || !attr_set[dev].load(std::memory_order_relaxed)) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias, kW8, kGS>),
+        reinterpret_cast<const void*>(&w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias, kW8, kGS, kReq>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
     if (e != hipSuccess) return e;
     if (cacheable) attr_set[dev].store(true, std::memory_order_relaxed);
   }
   const int64_t blocks = (N / BN) * ((M + BM - 1) / BM);
-  hipLaunchKernelGGL((w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias, kW8, kGS>),
-                     dim3((unsigned)blocks), dim3(64 * WGN * WGM), lds, st, Xq, xs, Wq, ws, bias, M, N, K, Y, ldy);
+  hipLaunchKernelGGL((w4a4_gemm_kernel<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kGelu, kBias, kW8, kGS, kReq>),
+                     dim3((unsigned)blocks), dim3(64 * WGN * WGM), lds, st, Xq, xs, Wq, ws, bias, M, N, K, Y, ldy, nq);
   return hipGetLastError();
 }
 
@@ -736,6 +797,42 @@ hipError_t launch_w4a4_gemm_grouped(const uint8_t* Xq, const float* xs, const ui
   if (group == 128) return launch_grouped<1>(Xq, xs, Wq, ws, bias, M, N, K, gelu, Y, bf16_out, ldy, st);
   if (group == 256) return launch_grouped<2>(Xq, xs, Wq, ws, bias, M, N, K, gelu, Y, bf16_out, ldy, st);
   return launch_grouped<4>(Xq, xs, Wq, ws, bias, M, N, K, gelu, Y, bf16_out, ldy, st);
+}
+
+namespace {
+
+__global__ void zero_counters_kernel(unsigned* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+template <int kReq, bool kGelu, bool kBias>
+hipError_t launch_requant_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
+                            int64_t M, int64_t K, void* Y, int64_t ldy, NextQuant nq, hipStream_t st) {
+  const int64_t stripes = (M + 127) / 128;
+  hipLaunchKernelGGL(zero_counters_kernel, dim3((unsigned)((stripes + 255) / 256)), dim3(256), 0, st, nq.counters,
+                     stripes);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_t<128, 128, 2, 2, 64, QV_STAGES, true, kGelu, kBias, false, 0, kReq>(Xq, xs, Wq, ws, bias, M, kReq,
+                                                                                   K, Y, ldy, st, nq);
+}
+
+}  // namespace
+
+hipError_t launch_w4a4_gemm_requant(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws,
+                                    const float* bias, int64_t M, int64_t N, int64_t K, bool gelu, void* Y,
+                                    int64_t ldy, const float* mult_next, uint8_t* q_next, float* scale_next,
+                                    unsigned* counters, hipStream_t st) {
+  const NextQuant nq{mult_next, q_next, scale_next, counters};
+#define QV_R(W, G, B) launch_requant_t<W, G, B>(Xq, xs, Wq, ws, bias, M, K, Y, ldy, nq, st)
+  if (N == 4096) {
+    if (bias) return gelu ? QV_R(4096, true, true) : QV_R(4096, false, true);
+    return gelu ? QV_R(4096, true, false) : QV_R(4096, false, false);
+  }
+  if (bias) return gelu ? QV_R(1024, true, true) : QV_R(1024, false, true);
+  return gelu ? QV_R(1024, true, false) : QV_R(1024, false, false);
+#undef QV_R
 }
 
 hipError_t launch_w8a8_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,

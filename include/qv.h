@@ -122,6 +122,33 @@ qv_status qv_w4a4_linear(const void* X, qv_dtype x_dtype, int64_t M, int64_t K, 
                          const float* bias, int64_t N, qv_epilogue epi, void* Y, qv_dtype y_dtype,
                          int64_t ldy, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Bytes of workspace qv_w4a4_gemm_requant needs for M rows: one counter per 128-row stripe,
+ * rounded up to 256 bytes (0 for invalid sizes). */
+size_t qv_w4a4_gemm_requant_workspace_size(int64_t M);
+
+/*
+ * qv_w4a4_gemm_requant -- qv_w4a4_gemm with bf16 outputs that also prepares the next linear's
+ * input: every output row is rotated, smoothed and quantized exactly as qv_hadamard_smooth_quant
+ * would do to Y, without a second pass over Y in HBM.  This is the MLP's fc1 -> GELU -> H_4096 ->
+ * int4 step ([P4] 预全局旋转 and 后局部平滑 applied to the next layer's input, 训练后量化（PTQ）; the
+ * intermediate is bf16, rounded to nearest even, as qv_w4a4_gemm stores it).
+ *   Xq, x_scale, Wq, w_scale, bias, M, K, epi   as for qv_w4a4_gemm.
+ *   N               1024 or 4096: the output width, which is the next layer's Hadamard width.
+ *   Y               [M][ldy] bf16 outputs, as qv_w4a4_gemm writes them (they are also read back).
+ *   inv_smooth_next [N] fp32 factors of the next layer (1 / smoothing), NULL = ones.
+ *   Xq_next         [M][N/2] packed int4 codes;  x_scale_next [M] fp32 per-row scales (outputs),
+ *                   identical to qv_hadamard_smooth_quant(Y, bf16, M, N, ldy, inv_smooth_next, ...).
+ *   workspace       at least qv_w4a4_gemm_requant_workspace_size(M) bytes, 256-byte aligned, cleared
+ *                   by the call itself (a fill kernel) and reused freely by later calls.
+ * The tiles of a 128-row stripe finish in any order; the block that finishes a stripe's last
+ * tile quantizes the stripe's rows after an agent-scope acquire that pairs with every tile's
+ * release.  No block waits for another.
+ */
+qv_status qv_w4a4_gemm_requant(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq, const float* w_scale,
+                               const float* bias, int64_t M, int64_t N, int64_t K, qv_epilogue epi, void* Y,
+                               int64_t ldy, const float* inv_smooth_next, uint8_t* Xq_next, float* x_scale_next,
+                               void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Bytes of the static device scratch array behind qv_w4a4_linear_noalloc, one copy per GPU. */
 #define QV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 

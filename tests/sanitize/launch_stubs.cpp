@@ -41,5 +41,10 @@ hipError_t launch_smooth_calibrate(const void*, bool, int64_t, int64_t, const vo
 }
 
 hipError_t noalloc_scratch(void**, size_t*) { return stub(); }
+hipError_t launch_w4a4_gemm_requant(const uint8_t*, const float*, const uint8_t*, const float*, const float*, int64_t,
+                                    int64_t, int64_t, bool, void*, int64_t, const float*, uint8_t*, float*, unsigned*,
+                                    hipStream_t) {
+  return stub();
+}
 
 }  // namespace qv

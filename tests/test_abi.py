@@ -204,6 +204,36 @@ def test_noalloc_linear_argument_errors(L):
     assert na(M=1 << 30, K=4096) == QV_ERR_WORKSPACE
 
 
+def test_gemm_requant_argument_errors(L):
+    """The GEMM that also quantizes its output for the next layer: the GEMM's rules, bf16 outputs,
+    N equal to a Hadamard width, its own outputs and counter workspace."""
+    assert L.qv_w4a4_gemm_requant_workspace_size(1) == 256
+    assert L.qv_w4a4_gemm_requant_workspace_size(128 * 64) == 256
+    assert L.qv_w4a4_gemm_requant_workspace_size(128 * 64 + 1) == 512
+    assert L.qv_w4a4_gemm_requant_workspace_size(-1) == 0
+    assert L.qv_w4a4_gemm_requant_workspace_size(1 << 62) == 0
+    need = L.qv_w4a4_gemm_requant_workspace_size(16)
+
+    def rq(M=16, N=4096, K=1024, ldy=4096, Xq=P, Y=P, inv=None, q=P, s=P, ws=P, wsb=need, epi=1):
+        return L.qv_w4a4_gemm_requant(Xq, P, P, P, None, M, N, K, epi, Y, ldy, inv, q, s, ws, wsb, None)
+
+    assert rq(M=0) == QV_OK
+    assert rq(N=2048, ldy=2048) == QV_ERR_UNSUPPORTED     # not a Hadamard width of the next layer
+    assert rq(N=1024, ldy=1024, K=1000) == QV_ERR_UNSUPPORTED
+    assert rq(Xq=None) == QV_ERR_NULL
+    assert rq(q=None) == QV_ERR_NULL
+    assert rq(s=None) == QV_ERR_NULL
+    assert rq(q=P_MIS) == QV_ERR_ALIGN
+    assert rq(s=P_MIS) == QV_ERR_ALIGN
+    assert rq(inv=P_MIS) == QV_ERR_ALIGN
+    assert rq(ldy=4100) == QV_ERR_ALIGN                   # bf16 row stride of 8200 bytes
+    assert rq(ldy=4000) == QV_ERR_SHAPE
+    assert rq(ws=None) == QV_ERR_WORKSPACE
+    assert rq(wsb=need - 1) == QV_ERR_WORKSPACE
+    assert rq(ws=P + 16) == QV_ERR_ALIGN
+    assert rq(epi=2) == QV_ERR_DTYPE
+
+
 def test_calibrate_argument_errors(L):
     f = ctypes.c_float
 
