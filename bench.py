@@ -394,8 +394,8 @@ def main():
     wq_bytes = sum(L.Wq.numel() + 4 * L.ws.numel() for L in layers)
     bf16_w_bytes = sum(2 * L.lin.N * L.lin.K for L in layers)
 
-    gemm_hash = kernel_source_hash(["w4a4_gemm.hip"])
-    rq_hash = kernel_source_hash(["rotate_quant.hip", "fwht_regs.h"])
+    gemm_hash = kernel_source_hash(["w4a4_gemm.hip", "rq_mfma.h", "fwht_regs.h"])
+    rq_hash = kernel_source_hash(["rotate_quant.hip", "rq_mfma.h", "fwht_regs.h"])
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
