@@ -355,23 +355,37 @@ def main():
     sclk = sample_clock(step, torch)
 
     # ---------------------------------------------------------------- per-kernel times (HIP events)
-    # Events on the library's stream bracket back-to-back launches with no event between them (an
-    # event between two kernels adds a dispatch gap of a few microseconds to the pair it separates).
-    #   * kernel averages: every layer's launch of that kernel in step order, repeated; the
-    #     rotate-quantize groups start after a cache flush;
-    #   * per linear: the launches of that linear in every block, back to back (one launch per group
-    #     when the workload has one block), repeated.
+    # Kernel durations in the context of the step: instrumented steps, after the timed ones, record
+    # an event before and after every launch on the library's stream, so each rotate-quantize runs
+    # after the previous layer's GEMM (its input cold in HBM, its codes read by the next GEMM) exactly
+    # as inside a timed step.  An event adds a dispatch latency of a few microseconds to the interval
+    # it opens, so these durations are slight upper bounds; the rocprofv3 kernel trace of the same
+    # command gives the kernels' own durations.  The per-linear GEMM figures also time back-to-back
+    # launches of one linear across the blocks, with no event in between.
     print("bench: per-kernel timing", file=sys.stderr, flush=True)
     reps = max(3, 60 // wl.blocks)
     launch_k1 = lambda L: qv.qv_hadamard_smooth_quant(L.X, L.inv, L.Xq, L.xs, stream)
     launch_k2 = lambda L: qv.qv_w4a4_gemm(L.Xq, L.xs, L.Wq, L.ws, None, L.Y, L.lin.epi, stream)
 
-    def all_layers(launch):
-        return lambda: [launch(L) for L in layers]
-
+    inst_steps = max(2, 96 // len(layers))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(inst_steps * len(layers))]
     step()
-    k1_t = sum(timer(all_layers(launch_k1), cold=True) for _ in range(reps)) / (reps * len(layers))
-    k2_t = sum(timer(all_layers(launch_k2)) for _ in range(reps)) / (reps * len(layers))
+    for i, e in enumerate(evs):
+        L = layers[i % len(layers)]
+        e[0].record(stream)
+        launch_k1(L)
+        e[1].record(stream)
+        launch_k2(L)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    k1_ts, k2_ts = {}, {}
+    for i, e in enumerate(evs):
+        name = layers[i % len(layers)].lin.name
+        k1_ts.setdefault(name, []).append(e[0].elapsed_time(e[1]) * 1e-3)
+        k2_ts.setdefault(name, []).append(e[1].elapsed_time(e[2]) * 1e-3)
+    n_launch = len(evs)
+    k1_t = sum(sum(v) for v in k1_ts.values()) / n_launch
+    k2_t = sum(sum(v) for v in k2_ts.values()) / n_launch
     k1_bytes = sum(rq_bytes(L) for L in layers) / len(layers)
     k2_ops = ops_per_step / len(layers)
     k2_tops = k2_ops / k2_t / 1e12
@@ -381,16 +395,19 @@ def main():
     for lin in wl.linears:
         group = [L for L in layers if L.lin.name == lin.name]
         g = [timer(lambda: [launch_k2(L) for L in group]) / len(group) for _ in range(reps)]
-        r = [timer(lambda: [launch_k1(L) for L in group], cold=True) / len(group) for _ in range(reps)]
-        gs, rs = sum(g) / len(g), sum(r) / len(r)
+        r1, r2 = k1_ts[lin.name], k2_ts[lin.name]
+        rs, gs = sum(r1) / len(r1), sum(r2) / len(r2)
+        gb = sum(g) / len(g)
         b1 = rq_bytes(group[0])
-        kernels[lin.name] = {"K": lin.K, "N": lin.N, "launches_per_group": len(group),
-                             "rotate_quant_us": round(1e6 * rs, 2), "rotate_quant_us_p10_p50_p90": pct(r),
+        ops = 2.0 * M * lin.N * lin.K
+        kernels[lin.name] = {"K": lin.K, "N": lin.N, "launches": len(r1),
+                             "rotate_quant_us": round(1e6 * rs, 2), "rotate_quant_us_p10_p50_p90": pct(r1),
                              "rotate_quant_GBps": round(b1 / rs / 1e9, 1),
                              "rotate_quant_frac": round(b1 / rs / 1e9 / PEAK_HBM_GBPS, 4),
-                             "gemm_us": round(1e6 * gs, 2), "gemm_us_p10_p50_p90": pct(g),
-                             "gemm_TOPS": round(2.0 * M * lin.N * lin.K / gs / 1e12, 1),
-                             "gemm_frac": round(2.0 * M * lin.N * lin.K / gs / 1e12 / PEAK_INT8_TOPS, 4)}
+                             "gemm_us": round(1e6 * gs, 2), "gemm_us_p10_p50_p90": pct(r2),
+                             "gemm_TOPS": round(ops / gs / 1e12, 1), "gemm_frac": round(ops / gs / 1e12 / PEAK_INT8_TOPS, 4),
+                             "gemm_us_back_to_back": round(1e6 * gb, 2),
+                             "gemm_TOPS_back_to_back": round(ops / gb / 1e12, 1)}
     wq_bytes = sum(L.Wq.numel() + 4 * L.ws.numel() for L in layers)
     bf16_w_bytes = sum(2 * L.lin.N * L.lin.K for L in layers)
 
@@ -414,12 +431,12 @@ def main():
         "rotate_quant_roofline": {"kernel": "rotate_quant", "bound": "hbm", "achieved": round(k1_gbps, 1),
                                   "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(k1_gbps / PEAK_HBM_GBPS, 4),
                                   "traffic": read_traffic("rotate_quant", rq_hash, wl.name),
-                                  "avg_launch_us": round(1e6 * k1_t, 3), "bytes_per_launch": k1_bytes,
-                                  "cold": f"a {FLUSH_BYTES >> 20} MiB scratch fill before each timed group"},
+                                  "avg_launch_us": round(1e6 * k1_t, 3), "bytes_per_launch": k1_bytes},
         "kernels": kernels,
         "rotate_quant_share_of_linear_time": round(k1_t / (k1_t + k2_t), 4),
-        "kernel_timing": (f"HIP events around {reps} groups of back-to-back launches (all layers in step order "
-                          f"for the averages, one linear across the blocks per line of 'kernels')"),
+        "kernel_timing": (f"HIP events before and after each launch of {inst_steps} instrumented steps "
+                          f"({n_launch} launches of each kernel) after the timed ones; 'gemm_us_back_to_back': "
+                          f"events around {reps} groups of one linear's launches across the blocks"),
         "gfx_clock_MHz_under_load": sclk,
         "weights_resident": {"int4_bytes_with_scales": wq_bytes, "bf16_bytes": bf16_w_bytes,
                              "ratio": round(bf16_w_bytes / wq_bytes, 3)},
