@@ -57,8 +57,9 @@ WORKLOADS = {
         frames=8, in_dtype="bf16", out_dtype="bf16",
         linears=(Linear("qkv", 1024, 3072, EPI_NONE, 0, 1),)),
     "mlp_24frames": Workload(
-        "mlp_24frames", "fc1 1024->4096 + GELU -> H4096 requant -> fc2 4096->1024, 24 frames "
-        "(M=32976), bf16", frames=24, in_dtype="bf16", out_dtype="bf16",
+        "mlp_24frames", "fc1 1024->4096 + GELU -> bf16 -> width-4096 rotate-quantize -> fc2 4096->1024, "
+        "24 frames (M=32976), bf16 (two-call chain; qv_w4a4_gemm_requant fuses the requantization into fc1)",
+        frames=24, in_dtype="bf16", out_dtype="bf16",
         linears=(Linear("fc1", 1024, 4096, EPI_GELU, 0, 1), Linear("fc2", 4096, 1024, EPI_NONE, 0, 2)),
         chain_mlp=True),
     "block_32frames": Workload(
