@@ -152,25 +152,31 @@ __device__ __forceinline__ float gelu(float y) {
   return __builtin_fmaf(-(x * t), e, fmaxf(y, 0.0f));
 }
 
-// LDS of a block: the stage ring (reused for output staging in the epilogue), then the tile's
-// BN weight scales and BM activation scales, fetched by LDS-DMA when the tile starts.
-template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out>
+// LDS of a block: the stage ring (reused for output staging in the epilogue), then the tile's BN
+// bias values (when a bias is given), BN weight scales and BM activation scales, fetched by LDS-DMA
+// when the tile starts.
+template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, bool kBias>
 struct GemmLds {
   static constexpr size_t kStage = (size_t)STAGES * (BN + BM) * RB;
   static constexpr size_t kOut =
       (size_t)WGN * WGM * (BM / WGM) * ((BN / WGN) * (kBF16Out ? 2 : 4) + (kBF16Out ? 8 : 16));
-  static constexpr size_t kScaleOffset = kStage > kOut ? kStage : kOut;
+  static constexpr size_t kBiasOffset = kStage > kOut ? kStage : kOut;
+  static constexpr size_t kScaleOffset = kBiasOffset + (kBias ? 4 * (size_t)BN : 0);
   static constexpr size_t kTotal = kScaleOffset + 4 * (size_t)(BN + BM);
 };
 
-// Waves per SIMD the register allocation must allow (at most 128 registers per lane for 4):
-// 64 x 64 wave tiles with a 2-deep ring of 64-byte stages fit four 4-wave or two 8-wave blocks per
-// CU; a 3-deep ring leaves room for three 4-wave blocks; the 128-accumulator wave tiles and the
-// 128-byte stages allow two.
+// Waves per SIMD the register allocation must allow (at most 128 registers per lane for 4, 168
+// for 3): 64 x 64 wave tiles (64 accumulators per lane) with a 2-deep ring of 64-byte stages fit
+// four 4-wave or two 8-wave blocks per CU; a 3-deep ring leaves room for three 4-wave blocks;
+// 64 x 96 wave tiles (96 accumulators) allow three; 64 x 128 wave tiles and the 128-byte stages
+// allow two.
 template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, int kGS = 0>
 constexpr int waves_per_eu() {
   if (kGS > 0) return 2;  // group-wise scales: an fp32 accumulator beside the int32 one
-  return (RB == 128 || (BN / WGN) * (BM / WGM) > 4096) ? 2 : ((WGN * WGM == 8 || STAGES == 2) ? 4 : 3);
+  constexpr int kAcc = (BN / WGN) * (BM / WGM) / 64;
+  if (RB == 128 || kAcc > 96) return 2;
+  if (kAcc > 64) return 3;
+  return (WGN * WGM == 8 || STAGES == 2) ? 4 : 3;
 }
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -217,7 +223,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
   static_assert(kUnits % kThr == 0, "tile must split evenly over the waves");
   static_assert(STAGES >= 2 && (STAGES - 2) * kLoads < 64, "pipeline depth");
   static_assert(kGS == 0 || (!kW8 && RB == 64), "group-wise scales: int4 operands, 128-code stages");
-  static_assert((BN + BM) % 64 == 0, "whole waves of scale loads");
+  static_assert((BN + BM) % 64 == 0 && BN % 64 == 0, "whole waves of scale and bias loads");
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
   const int tid = threadIdx.x;
@@ -325,7 +331,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
   // loads, so the first iteration's vmcnt wait covers them.
   // Group-wise scales: the same for every group g, into slots g (BN + BM) + i, from column g of the
   // [rows][groups] scale matrices.
-  float* const scales = reinterpret_cast<float*>(lds + GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out>::kScaleOffset);
+  using Lds = GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kBias>;
+  float* const scales = reinterpret_cast<float*>(lds + Lds::kScaleOffset);
+  float* const bias_lds = reinterpret_cast<float*>(lds + Lds::kBiasOffset);
   const int groups = kGS > 0 ? (int)(K / (128 * kGS)) : 1;  // groups of 128 kGS channels
   for (int g = 0; g < groups; ++g) {
 #pragma unroll
@@ -345,6 +353,19 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
                                        4, 0, 0);
     }
   }
+  if constexpr (kBias) {
+    // The tile's BN bias values, so the epilogue reads them from LDS (no per-lane global addresses
+    // held across the K loop).
+#pragma unroll
+    for (int r = 0; r < (BN + kThr - 1) / kThr; ++r) {
+      if (kThr * r + 64 * wave >= BN) break;  // wave-uniform
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bias + n0 + tid + kThr * r),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                           reinterpret_cast<uintptr_t>(bias_lds + 64 * (wave + kWaves * r))),
+                                       4, 0, 0);
+    }
+  }
+  (void)bias_lds;
   if constexpr (QV_DMA) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
@@ -501,7 +522,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
     if constexpr (kGS == 0) { sw[0] = sw4[a][vg].x; sw[1] = sw4[a][vg].y; sw[2] = sw4[a][vg].z; sw[3] = sw4[a][vg].w; }
     float bb[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (kBias) {
-      const float4 b4 = *reinterpret_cast<const float4*>(bias + n0 + wn * WN + 32 * a + 8 * vg + 4 * h);
+      const float4 b4 = *reinterpret_cast<const float4*>(bias_lds + wn * WN + 32 * a + 8 * vg + 4 * h);
       bb[0] = b4.x; bb[1] = b4.y; bb[2] = b4.z; bb[3] = b4.w;
     }
 #pragma unroll
@@ -625,13 +646,13 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BN, BM, WGN, WGM, RB, STAGES, kG
     constexpr int LA = kReq == 1024 ? 8 : 16;
     using RQ = MfmaRowQuant<kReq, 4, LA>;
     using RL = typename RQ::L;
-    static_assert(RL::kTableRows * kCmStride * 4 <= (int)GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out>::kScaleOffset,
+    static_assert(RL::kTableRows * kCmStride * 4 <= (int)GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kBias>::kScaleOffset,
                   "factor table fits the stage ring");
     static_assert(BM % (kWaves * RL::kRowsPerWave) == 0, "whole row groups per wave");
     // Every wave's output stores are complete and visible at agent scope, then one increment per block.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
-    int* const flag = reinterpret_cast<int*>(lds + GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out>::kScaleOffset);
+    int* const flag = reinterpret_cast<int*>(lds + GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kBias>::kScaleOffset);
     if (tid == 0) {
       const unsigned done = __hip_atomic_fetch_add(nq.counters + tile_m, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       *flag = (done == (unsigned)(tiles_n - 1)) ? 1 : 0;
@@ -669,7 +690,7 @@ template <int BN, int BM, int WGN, int WGM, int RB, int STAGES, bool kBF16Out, b
           int kGS = 0, int kReq = 0>
 hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, const float* bias,
                     int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st, NextQuant nq = {}) {
-  using Lds = GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out>;
+  using Lds = GemmLds<BN, BM, WGN, WGM, RB, STAGES, kBF16Out, kBias>;
   // Group-wise scales take one (BN + BM)-float slot per group, at most kMaxGroups of them.
   const size_t lds = kGS > 0 ? Lds::kScaleOffset + 4 * (size_t)(BN + BM) * (size_t)(K / (128 * kGS)) : Lds::kTotal;
   constexpr size_t kLdsMax = kGS > 0 ? Lds::kScaleOffset + 4 * (size_t)(BN + BM) * kMaxGroups : Lds::kTotal;
@@ -704,10 +725,17 @@ hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const
 //      per SIMD (~200 registers; two blocks per CU).  On the 100-frame layers (M = 137400) it
 //      measured 1-5 % faster than configuration 0 on every linear (proj 4.5 %, fc2 2.6 %, qkv 1.9 %,
 //      fc1 1.0 %); a 3-deep ring or 256-code stages on the same tile did not help.
+//   6: 128 x 192, 2 x 2 waves of 64 x 96: 4.17 widening instructions per MFMA, ~152 registers,
+//      three blocks per CU (3 x 41.5 KB of LDS).  It does 12-14 % more MFMA work per clock than
+//      configuration 5, but draws more power, so the power-limited clock settles 8-10 % lower
+//      (1.58-1.81 against 1.72-1.98 GHz).  Net, in GEMM-only runs with the two alternating on the
+//      100-frame layers, it was 2-5 % faster on every linear on two boxes (e.g. qkv 379-392 against
+//      396-400 us, proj 126-130 against 134-136, fc1 633-641 against 655-661, fc2 430 against
+//      438-440) and 3-4 % slower on a third; the outputs are identical.
 // A configuration whose BN does not divide N, and every fp32-output launch, uses configuration 0,
-// and so do int8 operands with configuration 5.
+// and so do int8 operands with configurations 5 and 6.
 #ifndef QV_TILE_CFG
-#define QV_TILE_CFG 5
+#define QV_TILE_CFG 6
 #endif
 
 template <int BN, int BM, int WGN, int WGM, bool kBF16Out, bool kGelu, bool kBias, bool kW8>
@@ -750,6 +778,8 @@ hipError_t launch_k(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const
   } else if constexpr (QV_TILE_CFG == 5 && !kW8) {
     // int8 operands keep configuration 0: their 128-byte stages would leave one block per CU here
     return QV_LAUNCH(128, 256, 2, 2);
+  } else if constexpr (QV_TILE_CFG == 6 && !kW8) {
+    return QV_LAUNCH(128, 192, 2, 2);
   }
   return QV_LAUNCH(128, 128, 2, 2);
 #undef QV_LAUNCH
