@@ -733,9 +733,15 @@ hipError_t launch_t(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const
 //      396-400 us, proj 126-130 against 134-136, fc1 633-641 against 655-661, fc2 430 against
 //      438-440) and 3-4 % slower on a third; the outputs are identical.
 // A configuration whose BN does not divide N, and every fp32-output launch, uses configuration 0,
-// and so do int8 operands with configurations 5 and 6.
+// and so do int8 operands with configurations 5 and 6 (int8 operands with bf16 outputs have their
+// own tile, QV_W8_TILE_CFG).
 #ifndef QV_TILE_CFG
 #define QV_TILE_CFG 6
+#endif
+// int8 operands with bf16 outputs: 5 = 128 x 256 tiles with 64-code stages (below), 0 = the
+// 128 x 128 tiles with 128-code stages of the other int8 launches.
+#ifndef QV_W8_TILE_CFG
+#define QV_W8_TILE_CFG 5
 #endif
 
 template <int BN, int BM, int WGN, int WGM, bool kBF16Out, bool kGelu, bool kBias, bool kW8>
@@ -743,8 +749,9 @@ hipError_t launch_cfg(const uint8_t* Xq, const float* xs, const uint8_t* Wq, con
                       int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
   // int4: 128 codes (64 bytes of every row) per stage; a 256-code stage variant is kept selectable
   // for measurements (it halves the barriers but its 64 KB ring leaves two blocks per CU).
-  // int8: 128 codes (128 bytes) per stage where K allows; 64-byte stages would carry half the MFMA
-  // work per barrier, and measured 5 % slower on the block despite the four blocks per CU.
+  // int8 on 128 x 128 tiles: 128 codes (128 bytes) per stage where K allows; 64-byte stages would
+  // carry half the MFMA work per barrier, and measured 5 % slower on the block despite the four
+  // blocks per CU.
   if constexpr (kW8) {
     if ((K % 128) == 0)
       return launch_t<BN, BM, WGN, WGM, 128, QV_STAGES_128, kBF16Out, kGelu, kBias, kW8>(Xq, xs, Wq, ws, bias, M, N, K,
@@ -767,6 +774,15 @@ hipError_t launch_k(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const
   if constexpr (!kBF16Out) {
     // fp32 outputs: the 256-wide tiles' output staging would not fit in LDS
     return QV_LAUNCH(128, 128, 2, 2);
+  } else if constexpr (kW8 && QV_W8_TILE_CFG == 5) {
+    // int8 operands with bf16 outputs: 128 x 256 tiles (4 waves of 64 x 128) with 64-code stages,
+    // two blocks per CU (2 x 49.5 KB of LDS, ~172 registers).  On the 100-frame layers this
+    // measured 3-5 % faster than 128 x 128 tiles with 128-code stages on the K = 1024 linears (qkv
+    // 500 against 524-547 us, proj 170-180 against 179-185, fc1 795-842 against 836-865; GEMM-only,
+    // alternating, two boxes) and level on fc2; a 3-deep ring, 128 x 192 and 256 x 128 tiles were
+    // no better.
+    return launch_t<128, 256, 2, 2, 64, QV_STAGES, kBF16Out, kGelu, kBias, kW8>(Xq, xs, Wq, ws, bias, M, N, K, Y,
+                                                                               ldy, st);
   } else if constexpr (QV_TILE_CFG == 1) {
     if (N % 256 == 0) return QV_LAUNCH(256, 256, 2, 4);
   } else if constexpr (QV_TILE_CFG == 2) {
