@@ -268,8 +268,11 @@ def test_gemm_many_tiles_per_block(qv, dev, K, epi, bias):
 
 
 @pytest.mark.parametrize("epi,out,bias,pad", [(0, "fp32", False, 0), (1, "fp32", False, 0), (0, "bf16", False, 0),
-                                              (1, "bf16", True, 64), (0, "fp32", True, 32)])
+                                              (1, "bf16", True, 64), (0, "fp32", True, 32), (0, "bf16", True, 0),
+                                              (1, "bf16", False, 8)])
 def test_gemm_epilogue_parity(qv, dev, epi, out, bias, pad):
+    """Every epilogue instance (GELU or not, bias or not, fp32 or bf16 outputs) on a ragged row count
+    (1375 rows: a partial last tile for every tile height) against the oracle."""
     M, N, K = 1375, 384, 1024
     X = synth.vggt_activations(M, K, seed=5, dtype="bf16")
     W = synth.weights(N, K, seed=6)

@@ -139,7 +139,7 @@ def test_gemm8_extreme_codes(qv, dev):
 
 
 @pytest.mark.parametrize("epi,out,bias,pad", [(0, "fp32", False, 0), (1, "fp32", True, 0), (1, "bf16", False, 0),
-                                              (0, "bf16", True, 64)])
+                                              (0, "bf16", True, 64), (1, "bf16", True, 0), (0, "bf16", False, 8)])
 def test_gemm8_epilogue_parity(qv, dev, epi, out, bias, pad):
     M, N, K = 1375, 384, 1024
     X = synth.vggt_activations(M, K, seed=15, dtype="bf16")
