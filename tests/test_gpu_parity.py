@@ -286,6 +286,31 @@ def test_gemm_epilogue_parity(qv, dev, epi, out, bias, pad):
     print(f"epilogue epi={epi} out={out} bias={bias}: max rel err {worst:.2e}")
 
 
+@pytest.mark.parametrize("K,dtype", [(1024, "bf16"), (4096, "bf16"), (1024, "fp32")])
+def test_row_ranges_are_independent(qv, dev, K, dtype):
+    """Rows are independent through both online steps: calls on row ranges give bit-identical codes,
+    scales and outputs to one call over all rows.  The split offsets are multiples of 4 rows (the
+    scale vectors' 16-byte alignment) and of no tile height, so a caller may split M into chunks."""
+    M, N = 3000, 384
+    X = synth.vggt_activations(M, K, seed=21, dtype=dtype)
+    W = synth.weights(N, K, seed=22)
+    Xd, Wd = to_dev(X, dtype, dev), to_dev(W, "fp32", dev)
+    Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    ws = torch.empty((N,), dtype=torch.float32, device=dev)
+    qv.qv_pack_weights(Wd, None, Wq, ws)
+    whole = [torch.empty((M, K // 2), dtype=torch.uint8, device=dev), torch.empty((M,), dtype=torch.float32, device=dev),
+             torch.empty((M, N), dtype=torch.bfloat16, device=dev)]
+    parts = [torch.empty_like(t) for t in whole]
+    qv.qv_hadamard_smooth_quant(Xd, None, whole[0], whole[1])
+    qv.qv_w4a4_gemm(whole[0], whole[1], Wq, ws, None, whole[2], 1)
+    for a, b in ((0, 4), (4, 1004), (1004, 2996), (2996, 3000)):
+        qv.qv_hadamard_smooth_quant(Xd[a:b], None, parts[0][a:b], parts[1][a:b])
+        qv.qv_w4a4_gemm(parts[0][a:b], parts[1][a:b], Wq, ws, None, parts[2][a:b], 1)
+    torch.cuda.synchronize()
+    for w, p_ in zip(whole, parts):
+        assert torch.equal(w.view(torch.uint8), p_.view(torch.uint8))
+
+
 # ---------------------------------------------------------------------------- whole layer
 
 @pytest.mark.parametrize("K", [1024, 4096])
