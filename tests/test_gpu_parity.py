@@ -311,6 +311,46 @@ def test_row_ranges_are_independent(qv, dev, K, dtype):
         assert torch.equal(w.view(torch.uint8), p_.view(torch.uint8))
 
 
+def test_concurrent_streams_match_one_stream(qv, dev):
+    """Two linears issued on two streams at once (each call on its caller's stream, kernels of both
+    in flight together) give the bit-identical codes, scales and outputs of the same calls issued
+    one after the other on one stream: the library keeps no per-call state outside its arguments."""
+    shapes = [(2000, 1024, 768, 1), (1500, 4096, 256, 0)]
+    inputs = []
+    for i, (M, K, N, epi) in enumerate(shapes):
+        X = to_dev(synth.vggt_activations(M, K, seed=30 + i, dtype="bf16"), "bf16", dev)
+        Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        ws = torch.empty((N,), dtype=torch.float32, device=dev)
+        qv.qv_pack_weights(to_dev(synth.weights(N, K, seed=40 + i), "fp32", dev), None, Wq, ws)
+        inputs.append((X, Wq, ws, epi))
+
+    def outputs():
+        return [(torch.empty((X.shape[0], X.shape[1] // 2), dtype=torch.uint8, device=dev),
+                 torch.empty((X.shape[0],), dtype=torch.float32, device=dev),
+                 torch.empty((X.shape[0], Wq.shape[0]), dtype=torch.bfloat16, device=dev)) for X, Wq, _, _ in inputs]
+
+    def run(i, o, stream):
+        X, Wq, ws, epi = inputs[i]
+        qv.qv_hadamard_smooth_quant(X, None, o[0], o[1], stream)
+        qv.qv_w4a4_gemm(o[0], o[1], Wq, ws, None, o[2], epi, stream)
+
+    torch.cuda.synchronize()
+    one = outputs()
+    for rep in range(3):
+        for i in range(len(inputs)):
+            run(i, one[i], torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    two = outputs()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for i in range(len(inputs)):
+            run(i, two[i], streams[i])
+    torch.cuda.synchronize()
+    for a, b in zip(one, two):
+        for x, y in zip(a, b):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
 # ---------------------------------------------------------------------------- whole layer
 
 @pytest.mark.parametrize("K", [1024, 4096])
